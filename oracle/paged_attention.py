@@ -1,0 +1,295 @@
+"""Plain fp64 CPU oracle of paged decode attention and of the KV cache write.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+What is computed, and where the pages define it:
+
+* Paged KV cache.  The K/V vectors of a sequence live in fixed-size blocks of
+  `block_size` tokens; a per-sequence block table maps logical block j (tokens
+  j*BS .. j*BS+BS-1) to a physical block of the pool; -1 marks an unallocated
+  entry.  ("How does paged attention work (in detail)", section 2 and 4.1;
+  "Paged attention" wiki, decode-path example; vLLM paper summary, section 2.)
+* Cache layouts (this library's): k_cache [NB, KVH, BS, D] and
+  v_cache [NB, KVH, D, BS]; the V tile is the value-cache layout of the vLLM
+  "Paged Attention" design page (section "Input parameters").
+* Scores: x_t = scale * <q, k_t> over the whole head ("Paged Attention" design
+  page, section "QK").
+* Softmax: m = max_t x_t, f_t = exp(x_t - m), l = sum_t f_t, p = f / l
+  (design page, section "Softmax", the displayed formula).
+* Tokens at positions >= context_len do not take part (design page, section
+  "Softmax", qk_max and logits: the mask token_idx >= context_len).
+* Output: out = sum_t p_t * v_t (design page, sections "Value" and "LV").
+* Query head h reads kv head h // (H / KVH) (contiguous groups; the pages only
+  name num_kv_heads / kv_head_idx).
+
+Readings where the pages are silent (each also listed in the design notes):
+  - context_lens counts the tokens attended; the new token of a decode step is
+    written first and attended with context_len + 1.
+  - the 1e-6 added to the exp sum on the design page is not part of the
+    definition (l >= 1 always, since the max term is e^0).
+  - an empty context gives a zero output.
+  - a partition p of P tokens yields (m_p, l_p, o_p) with o_p normalised;
+    merging uses M = max m_p, l = sum l_p e^(m_p - M),
+    out = sum (l_p e^(m_p - M) / l) o_p.  This is the softmax definition
+    split over disjoint token sets; the pages do not describe the merge.
+  - a block id outside [0, num_blocks) inside the context, or a context
+    longer than the table, is a caller error (ValueError here).
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Tuple
+
+import numpy as np
+
+from .formats import e4m3fn_encode, inv_scale_f32, to_f64
+
+
+# ----------------------------------------------------------------------------
+# indexing (block table -> slots)
+
+def num_logical_blocks(context_len: int, block_size: int) -> int:
+    """Logical blocks holding context_len tokens: ceil(L / BS)."""
+    return -(-int(context_len) // int(block_size))
+
+
+def validate(block_table: np.ndarray, context_lens: np.ndarray, block_size: int,
+             num_blocks: int, num_heads: int = 1, num_kv_heads: int = 1) -> None:
+    """Raise ValueError on inputs the method leaves undefined."""
+    if num_kv_heads <= 0 or num_heads % num_kv_heads != 0:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    S, MB = block_table.shape
+    if context_lens.shape != (S,):
+        raise ValueError("context_lens must have one entry per sequence")
+    for s in range(S):
+        L = int(context_lens[s])
+        if L < 0 or L > MB * block_size:
+            raise ValueError(f"sequence {s}: context length {L} outside [0, {MB * block_size}]")
+        for j in range(num_logical_blocks(L, block_size)):
+            b = int(block_table[s, j])
+            if b < 0 or b >= num_blocks:
+                raise ValueError(f"sequence {s}: logical block {j} maps to {b}, "
+                                 f"not a block of the pool [0, {num_blocks})")
+
+
+def token_slots(block_table_row: np.ndarray, context_len: int, block_size: int
+                ) -> List[Tuple[int, int]]:
+    """(physical block, offset in block) of logical positions 0..L-1:
+    position t sits in logical block t // BS at offset t % BS ("How does paged
+    attention work", section 4.1, steps 2 and 5)."""
+    return [(int(block_table_row[t // block_size]), t % block_size)
+            for t in range(int(context_len))]
+
+
+def next_slot(block_table_row: np.ndarray, context_len: int, block_size: int) -> int:
+    """Slot of the token written at position context_len: the physical block
+    that logical block context_len // BS maps to, times BS, plus the offset
+    context_len % BS.  Raises if that logical block is unallocated (the block
+    manager must map it first, as in the vLLM paper summary's second decode
+    step)."""
+    j = int(context_len) // block_size
+    if j >= len(block_table_row) or int(block_table_row[j]) < 0:
+        raise ValueError("logical block of the new token is not allocated")
+    return int(block_table_row[j]) * block_size + int(context_len) % block_size
+
+
+# ----------------------------------------------------------------------------
+# gather + attention
+
+def gather_kv(k_cache: np.ndarray, v_cache: np.ndarray, block_table_row: np.ndarray,
+              context_len: int, block_size: int, kv_head: int):
+    """Contiguous fp64 K, V [L, D] of one sequence and kv head, read through
+    the block table.  k_cache/v_cache are fp64 (already dequantised)."""
+    L = int(context_len)
+    nblk = num_logical_blocks(L, block_size)
+    ids = np.asarray(block_table_row[:nblk], dtype=np.int64)
+    K = k_cache[ids, kv_head]                      # [nblk, BS, D]
+    V = v_cache[ids, kv_head]                      # [nblk, D, BS]
+    D = K.shape[-1]
+    K = K.reshape(nblk * block_size, D)[:L]
+    V = np.transpose(V, (0, 2, 1)).reshape(nblk * block_size, D)[:L]
+    return K, V
+
+
+def softmax_stats(x: np.ndarray):
+    """(m, l, p) of the design page's softmax definition."""
+    m = np.max(x)
+    f = np.exp(x - m)
+    l = np.sum(f)
+    return m, l, f / l
+
+
+def _dequant(cache: np.ndarray, fmt: str, scale: float) -> np.ndarray:
+    c = to_f64(cache, fmt)
+    if fmt == "e4m3fn":
+        c = c * np.float64(np.float32(scale))
+    return c
+
+
+def _chunk_cache(cache, fmt, scale, ids, kv_head):
+    """Dequantised tiles of the listed physical blocks for one kv head."""
+    return _dequant(np.ascontiguousarray(cache[ids, kv_head]), fmt, scale)
+
+
+def decode_sequence(q_s: np.ndarray, k_cache, v_cache, table_row, context_len: int,
+                    scale: float, num_kv_heads: int, block_size: int, cache_fmt: str,
+                    k_scale: float = 1.0, v_scale: float = 1.0,
+                    heads=None, return_probs: bool = False):
+    """Decode attention of one sequence.  q_s is fp64 [H, D]; the caches are
+    raw arrays in cache_fmt.  Returns out [len(heads), D] fp64 (and the
+    softmax weights per head when return_probs)."""
+    H, D = q_s.shape
+    G = H // num_kv_heads
+    heads = range(H) if heads is None else heads
+    L = int(context_len)
+    nblk = num_logical_blocks(L, block_size)
+    ids = np.asarray(table_row[:nblk], dtype=np.int64)
+    out = np.zeros((len(heads), D), dtype=np.float64)
+    probs = []
+    cached = {}
+    for i, h in enumerate(heads):
+        if L == 0:
+            probs.append(np.zeros(0))
+            continue
+        kvh = h // G
+        if kvh not in cached:
+            Kt = _chunk_cache(k_cache, cache_fmt, k_scale, ids, kvh)      # [nblk, BS, D]
+            Vt = _chunk_cache(v_cache, cache_fmt, v_scale, ids, kvh)      # [nblk, D, BS]
+            K = Kt.reshape(nblk * block_size, D)[:L]
+            V = np.transpose(Vt, (0, 2, 1)).reshape(nblk * block_size, D)[:L]
+            cached = {kvh: (K, V)}
+        K, V = cached[kvh]
+        x = np.float64(np.float32(scale)) * (K @ q_s[h])
+        _, _, p = softmax_stats(x)
+        out[i] = p @ V
+        probs.append(p)
+    return (out, probs) if return_probs else out
+
+
+def paged_decode(q, k_cache, v_cache, block_table, context_lens, scale: float,
+                 num_kv_heads: int, block_size: int, q_fmt: str, cache_fmt: str,
+                 k_scale: float = 1.0, v_scale: float = 1.0, seqs=None, heads=None):
+    """out[s, h, :] for every (or the listed) sequence and head, fp64.
+
+    q [S, H, D] raw in q_fmt; caches raw in cache_fmt; block_table [S, MB]
+    int32; context_lens [S] int32."""
+    S, H, D = q.shape
+    NB = k_cache.shape[0]
+    validate(block_table, context_lens, block_size, NB, H, num_kv_heads)
+    seqs = range(S) if seqs is None else seqs
+    hs = list(range(H)) if heads is None else list(heads)
+    out = np.zeros((len(seqs), len(hs), D), dtype=np.float64)
+    for i, s in enumerate(seqs):
+        q_s = to_f64(q[s], q_fmt)
+        out[i] = decode_sequence(q_s, k_cache, v_cache, block_table[s], int(context_lens[s]),
+                                 scale, num_kv_heads, block_size, cache_fmt,
+                                 k_scale, v_scale, heads=hs)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# split-context partitions and their merge
+
+def partition_partials(q_s: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+                       partition_size: int):
+    """(m_p, l_p, o_p) over tokens [p*P, min((p+1)*P, L)) for one head;
+    q_s [D], K, V [L, D] fp64."""
+    L = K.shape[0]
+    x = np.float64(np.float32(scale)) * (K @ q_s)
+    res = []
+    for start in range(0, L, partition_size):
+        xs = x[start:start + partition_size]
+        m, l, p = softmax_stats(xs)
+        res.append((m, l, p @ V[start:start + partition_size]))
+    return res
+
+
+def merge_partials(partials) -> np.ndarray:
+    """Merge (m_p, l_p, o_p) triples: M = max m_p, l = sum l_p e^(m_p - M),
+    out = sum (l_p e^(m_p - M) / l) o_p.  Empty -> None (caller writes 0)."""
+    if not partials:
+        return None
+    M = max(m for m, _, _ in partials)
+    w = [l * math.exp(m - M) for m, l, _ in partials]
+    total = sum(w)
+    return sum((wi / total) * o for wi, (_, _, o) in zip(w, partials))
+
+
+def paged_decode_partitioned(q, k_cache, v_cache, block_table, context_lens, scale,
+                             num_kv_heads, block_size, q_fmt, cache_fmt, partition_size,
+                             k_scale=1.0, v_scale=1.0, seqs=None, heads=None):
+    """Per-partition triples and merged output.
+
+    Returns (out [S', H', D], partials) where partials[(s, h)] is the list of
+    (m_p, l_p, o_p) in partition order."""
+    S, H, D = q.shape
+    if partition_size <= 0 or partition_size % block_size != 0:
+        raise ValueError("partition size must be a positive multiple of the block size")
+    validate(block_table, context_lens, block_size, k_cache.shape[0], H, num_kv_heads)
+    G = H // num_kv_heads
+    seqs = range(S) if seqs is None else seqs
+    hs = list(range(H)) if heads is None else list(heads)
+    out = np.zeros((len(seqs), len(hs), D), dtype=np.float64)
+    parts = {}
+    for i, s in enumerate(seqs):
+        L = int(context_lens[s])
+        q_s = to_f64(q[s], q_fmt)
+        nblk = num_logical_blocks(L, block_size)
+        ids = np.asarray(block_table[s, :nblk], dtype=np.int64)
+        for j, h in enumerate(hs):
+            kvh = h // G
+            Kt = _chunk_cache(k_cache, cache_fmt, k_scale, ids, kvh)
+            Vt = _chunk_cache(v_cache, cache_fmt, v_scale, ids, kvh)
+            K = Kt.reshape(nblk * block_size, D)[:L]
+            V = np.transpose(Vt, (0, 2, 1)).reshape(nblk * block_size, D)[:L]
+            pp = partition_partials(q_s[h], K, V, scale, partition_size)
+            parts[(s, h)] = pp
+            merged = merge_partials(pp)
+            if merged is not None:
+                out[i, j] = merged
+    return out, parts
+
+
+# ----------------------------------------------------------------------------
+# cache write
+
+def cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, cache_fmt: str,
+                k_scale: float = 1.0, v_scale: float = 1.0):
+    """New caches after writing token i's K/V [KVH, D] to slot slot_mapping[i].
+
+    slot = physical block * BS + offset ("How does paged attention work",
+    section 4.1, step 5: the token's K/V goes to its position inside the
+    physical block); slot < 0 is skipped.  16-bit caches take the input bits
+    unchanged; an e4m3fn cache takes e4m3fn(clamp(fp32(x) * fp32(1/scale)))
+    (see formats.e4m3fn_encode).  Inputs are not modified."""
+    kc = k_cache.copy()
+    vc = v_cache.copy()
+    NB = kc.shape[0]
+    k_inv = inv_scale_f32(k_scale)
+    v_inv = inv_scale_f32(v_scale)
+    seen = set()
+    for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        if slot in seen:
+            raise ValueError(f"slot {slot} written twice")
+        seen.add(slot)
+        b, o = divmod(int(slot), block_size)
+        if b >= NB:
+            raise ValueError(f"slot {slot} is outside the pool")
+        if cache_fmt == "e4m3fn":
+            kk = e4m3fn_encode(to_f64(k[i], _fmt_of(k)).astype(np.float32), k_inv)
+            vv = e4m3fn_encode(to_f64(v[i], _fmt_of(v)).astype(np.float32), v_inv)
+        else:
+            kk, vv = k[i], v[i]
+        kc[b, :, o, :] = kk
+        vc[b, :, :, o] = vv
+    return kc, vc
+
+
+def _fmt_of(a: np.ndarray) -> str:
+    if a.dtype == np.float16:
+        return "f16"
+    if a.dtype == np.uint16:
+        return "bf16"
+    raise ValueError("new k/v must be f16 (np.float16) or bf16 (uint16 bits)")

@@ -1,0 +1,18 @@
+"""Seeded synthetic decode workloads shared by the tests, the benchmark and smoke().
+
+This package only draws inputs (random values, context lengths, block tables,
+slot mappings).  It holds none of the attention arithmetic: neither the GPU
+path nor the CPU oracle is imported here, and both consume what it returns.
+"""
+from .synth import (  # noqa: F401
+    Workload,
+    CONFIGS,
+    make,
+    worked_example,
+    llama7b_mha,
+    gqa,
+    long_context,
+    fp8_shared_prefix,
+    poison_unused_slots,
+    to_numpy_bits,
+)
