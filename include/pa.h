@@ -1,0 +1,176 @@
+/*
+ * pa.h — C ABI of the paged decode-attention library (libpa.so, HIP for gfx950).
+ *
+ * What the library computes (cited by page and section):
+ *   - Paged KV cache: K/V vectors live in fixed-size blocks of `block_size`
+ *     tokens scattered through a physical pool; a per-sequence block table maps
+ *     logical block j (tokens j*block_size .. j*block_size+block_size-1) to a
+ *     physical block; -1 marks an unallocated entry.
+ *     ("How does paged attention work (in detail)", sections 2 and 4.1;
+ *      "Paged attention" wiki, decode path and its example.)
+ *   - Decode attention: one query token per sequence attends, for every head,
+ *     over the sequence's whole context: x_t = scale * <q, k_t>, softmax
+ *     m = max x, f = exp(x - m), l = sum f, p = f / l, out = sum p_t v_t.
+ *     (vLLM "Paged Attention" design page, sections "QK", "Softmax", "Value",
+ *      "LV" and "Output".)
+ *   - Cache write: a new token's K/V goes to its slot inside a physical block.
+ *     ("How does paged attention work", section 4.1 step 5; vLLM paper summary,
+ *      section 3 "Decoding".)
+ *   - Split-context partitions whose partial results are merged
+ *     (the design page's max_num_partitions grid dimension and per-partition
+ *      output slot, section "Output"); the merge rule is derived from the
+ *      softmax definition.
+ *
+ * Layouts (row-major, element type `cache_dtype`):
+ *   k_cache [num_blocks, num_kv_heads, block_size, head_size]   token-major tile
+ *   v_cache [num_blocks, num_kv_heads, head_size, block_size]   dim-major tile
+ *   q       [num_seqs, num_heads, head_size] with row stride q_seq_stride
+ *   out     [num_seqs, num_heads, head_size] contiguous, element type q_dtype
+ *   block_table  [num_seqs, max_blocks_per_seq] int32
+ *   context_lens [num_seqs] int32: tokens attended by sequence s (positions
+ *                0 .. context_lens[s]-1).  A decode step writes the new token
+ *                at position L with pa_cache_write, then decodes with L + 1.
+ * Query head h reads kv head h / (num_heads / num_kv_heads).
+ *
+ * Element types: q/out f16 or bf16; caches f16, bf16 (same type as q) or
+ * fp8 e4m3fn (OCP) with one fp32 scale per cache: value = code * k_scale
+ * (resp. v_scale).  Scales are ignored for 16-bit caches.
+ *
+ * Ownership and execution: every array pointer is a device pointer owned by
+ * the caller; inputs are only read; only out, the caches (pa_cache_write) and
+ * the workspace arrays are written.  The library allocates nothing and keeps
+ * no state.  All calls are asynchronous on `stream` (a hipStream_t; NULL is
+ * the default stream); a PA_OK return means "launched", not "finished".
+ *
+ * Errors: arguments the host can check are checked before any launch and give
+ * a negative pa_status with nothing launched.  Errors only visible in device
+ * data (a block id outside [0, num_blocks) inside a context, a context longer
+ * than the table or than max_context_len, a negative context length) are not
+ * reported: the affected (sequence, head) output row is written as NaN and no
+ * address derived from the bad entry is read.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_F16 = 0,
+  PA_BF16 = 1,
+  PA_FP8_E4M3FN = 2
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  PA_ERR_SHAPE = -2,       /* a size is <= 0 or sizes are inconsistent      */
+  PA_ERR_UNSUPPORTED = -3, /* head size / block size / group not built      */
+  PA_ERR_DTYPE = -4,       /* element type combination not supported        */
+  PA_ERR_WORKSPACE = -5,   /* partition size or workspace invalid           */
+  PA_ERR_HIP = -6          /* the HIP runtime refused the launch            */
+} pa_status;
+
+/* Static text for a status code (never NULL). */
+const char* pa_status_string(int status);
+
+/* Version of this ABI (incremented on any signature change). */
+int pa_abi_version(void);
+
+/*
+ * pa_cache_write — store num_tokens new K/V vectors into their cache slots.
+ *   k, v          [num_tokens, num_kv_heads, head_size] (row stride
+ *                 kv_token_stride elements; heads contiguous), in_dtype.
+ *   slot_mapping  [num_tokens] int32: slot = physical_block * block_size +
+ *                 offset; a negative slot skips the token.
+ *   Writes k[i, h, :] to k_cache[slot / BS, h, slot % BS, :] and v[i, h, :]
+ *   to v_cache[slot / BS, h, :, slot % BS]; nothing else is written.
+ *   16-bit caches: cache_dtype == in_dtype, bits copied unchanged.
+ *   fp8 cache: code = e4m3fn(clamp(x * (1/scale), -448, 448)) rounded to
+ *   nearest even, with 1/scale computed once in fp32 on the host and the
+ *   product taken in fp32; NaN stays NaN.
+ *   Slots >= num_blocks * block_size are skipped (caller error); two tokens
+ *   with the same slot is a caller error (which one wins is unspecified).
+ * Supported: head_size in {64, 128}, block_size in {16, 32}.
+ */
+int pa_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                   const int32_t* slot_mapping, int32_t num_tokens,
+                   int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                   int64_t num_blocks, int64_t kv_token_stride,
+                   pa_dtype in_dtype, pa_dtype cache_dtype,
+                   float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_decode — decode attention over the paged cache in one pass.
+ *   out[s, h, :] = sum_t p_t * V_s[t, h / G, :] with p the softmax of
+ *   scale * <q[s, h, :], K_s[t, h / G, :]> over t < context_lens[s]
+ *   (G = num_heads / num_kv_heads); context_lens[s] == 0 gives zeros.
+ *   Entries of block_table past ceil(context_lens[s] / block_size) are never
+ *   read (they may be -1).  Deterministic: the same inputs give the same bits.
+ * Supported: head_size in {64, 128}; block_size in {16, 32}; G in [1, 16];
+ *   q_dtype in {f16, bf16}; cache_dtype == q_dtype or PA_FP8_E4M3FN.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, const int32_t* context_lens,
+              float scale, int32_t num_kv_heads, int32_t block_size,
+              int32_t num_seqs, int32_t num_heads, int32_t head_size,
+              int32_t max_blocks_per_seq, int64_t num_blocks, int64_t q_seq_stride,
+              pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale, float v_scale,
+              void* stream);
+
+/*
+ * Workspace of pa_decode_partitioned, in bytes, for
+ * NP = ceil(max_context_len / partition_size) partitions:
+ *   tmp_out    [num_seqs, num_heads, NP, head_size] fp32
+ *   max_logits [num_seqs, num_heads, NP] fp32
+ *   exp_sums   [num_seqs, num_heads, NP] fp32
+ * (three separate arrays; this returns their total).  0 on invalid sizes.
+ */
+size_t pa_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                    int32_t head_size, int32_t max_context_len,
+                                    int32_t partition_size);
+
+/*
+ * pa_decode_partitioned — split each context into partitions of
+ * partition_size tokens (a multiple of block_size) and write, for partition
+ * p < ceil(context_lens[s] / partition_size):
+ *   max_logits[s, h, p] = m_p = max of scale * <q, k_t> over the partition
+ *   exp_sums[s, h, p]   = l_p = sum_t exp(x_t - m_p)
+ *   tmp_out[s, h, p, :] = o_p = sum_t exp(x_t - m_p) v_t / l_p
+ * Partitions p >= that count are not written.  max_context_len bounds every
+ * context_lens[s] (a longer context gives a NaN row in pa_reduce) and sets
+ * the partition count NP = ceil(max_context_len / partition_size).
+ * Same support matrix as pa_decode.
+ */
+int pa_decode_partitioned(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* context_lens,
+                          float scale, int32_t num_kv_heads, int32_t block_size,
+                          int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                          int32_t max_blocks_per_seq, int64_t num_blocks,
+                          int64_t q_seq_stride, pa_dtype q_dtype, pa_dtype cache_dtype,
+                          float k_scale, float v_scale, int32_t partition_size,
+                          int32_t max_context_len, float* tmp_out, float* max_logits,
+                          float* exp_sums, void* stream);
+
+/*
+ * pa_reduce — merge the partitions written by pa_decode_partitioned:
+ *   M = max_p m_p, l = sum_p l_p exp(m_p - M),
+ *   out[s, h, :] = sum_p (l_p exp(m_p - M) / l) o_p      (p < NP_s)
+ * with NP_s = ceil(context_lens[s] / partition_size); context 0 gives zeros;
+ * NP_s > max_num_partitions or a NaN partial gives a NaN row.
+ *   out [num_seqs, num_heads, head_size] out_dtype (f16 or bf16).
+ */
+int pa_reduce(void* out, const float* tmp_out, const float* max_logits,
+              const float* exp_sums, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_heads, int32_t head_size, int32_t partition_size,
+              int32_t max_num_partitions, pa_dtype out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

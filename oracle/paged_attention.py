@@ -175,8 +175,8 @@ def paged_decode(q, k_cache, v_cache, block_table, context_lens, scale: float,
     int32; context_lens [S] int32."""
     S, H, D = q.shape
     NB = k_cache.shape[0]
-    validate(block_table, context_lens, block_size, NB, H, num_kv_heads)
-    seqs = range(S) if seqs is None else seqs
+    seqs = list(range(S)) if seqs is None else list(seqs)
+    validate(block_table[seqs], context_lens[seqs], block_size, NB, H, num_kv_heads)
     hs = list(range(H)) if heads is None else list(heads)
     out = np.zeros((len(seqs), len(hs), D), dtype=np.float64)
     for i, s in enumerate(seqs):
@@ -225,9 +225,9 @@ def paged_decode_partitioned(q, k_cache, v_cache, block_table, context_lens, sca
     S, H, D = q.shape
     if partition_size <= 0 or partition_size % block_size != 0:
         raise ValueError("partition size must be a positive multiple of the block size")
-    validate(block_table, context_lens, block_size, k_cache.shape[0], H, num_kv_heads)
+    seqs = list(range(S)) if seqs is None else list(seqs)
+    validate(block_table[seqs], context_lens[seqs], block_size, k_cache.shape[0], H, num_kv_heads)
     G = H // num_kv_heads
-    seqs = range(S) if seqs is None else seqs
     hs = list(range(H)) if heads is None else list(heads)
     out = np.zeros((len(seqs), len(hs), D), dtype=np.float64)
     parts = {}

@@ -1,0 +1,13 @@
+"""Paged decode attention for MI355X (gfx950): a C-ABI HIP library and its
+Python binding.  See include/pa.h for the ABI."""
+from .binding import (  # noqa: F401
+    EXPORTS,
+    PagedAttentionError,
+    cache_write,
+    decode,
+    decode_partitioned,
+    decode_partitioned_only,
+    lib,
+    partition_workspace,
+    reduce,
+)

@@ -1,0 +1,122 @@
+// KV cache write: store each new token's K and V into its slot.
+//
+// The slot of a token is physical_block * block_size + offset: the block
+// manager maps the token's logical block (position // block_size) to a
+// physical block and the token goes to its position inside it ("How does
+// paged attention work (in detail)", section 4.1; vLLM paper summary,
+// section 3 "Decoding").  K rows are contiguous in a K tile ([BS][D]); a V
+// row is a column of the V tile ([D][BS]).
+//
+// One thread per (token, kv head, 8 consecutive head dims): a 16-byte load
+// of k and of v, one 16-byte (8-byte for fp8) K store and 8 V element stores.
+//
+// fp8 caches store e4m3fn(clamp(x * inv_scale, +-448)) rounded to nearest
+// even, computed here with integer operations from the format definition
+// (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals
+// m * 2^-9, S.1111.111 = NaN, largest finite 448).
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+__device__ __forceinline__ uint32_t e4m3fn_encode(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  if (y != y) return sign | 0x7Fu;
+  float a = __builtin_fabsf(y);
+  a = a > 448.0f ? 448.0f : a;                 // saturate (also +-inf)
+  const uint32_t ua = __builtin_bit_cast(uint32_t, a);
+  const int e = (int)(ua >> 23) - 127;
+  if (e < -6) {
+    // below the smallest normal: quantum 2^-9; rint rounds half to even
+    const uint32_t mi = (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8 (8 = 2^-6)
+    return sign | mi;
+  }
+  // keep 3 mantissa bits, round half to even (carry may bump the exponent)
+  const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
+  const uint32_t e2 = (r >> 23) - 127u + 7u;
+  const uint32_t m3 = (r >> 20) & 7u;
+  return sign | (e2 << 3) | m3;
+}
+
+template <typename IT>
+__device__ __forceinline__ float in_elem(const u32x4_t& w, int j) {
+  if constexpr (__is_same(IT, F16)) return (j & 1) ? f16_hi(w[j >> 1]) : f16_lo(w[j >> 1]);
+  else return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+}
+
+template <typename IT, typename CT, int D, int BS>
+__global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams p) {
+  constexpr int CHUNKS = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * CHUNKS;
+  if (gid >= total) return;
+  const int c = (int)(gid % CHUNKS);
+  const int64_t th = gid / CHUNKS;
+  const int h = (int)(th % p.num_kv_heads);
+  const int t = (int)(th / p.num_kv_heads);
+  const int32_t slot = p.slot_mapping[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / BS;
+  const int off = slot % BS;
+  if (blk >= p.num_blocks) return;
+
+  const int64_t src = (int64_t)t * p.kv_token_stride + (int64_t)h * D + c * 8;
+  const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(p.k) + src);
+  const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(p.v) + src);
+  const int64_t tile = (blk * p.num_kv_heads + h) * (int64_t)(BS * D);   // elements
+
+  if constexpr (CT::kBytes == 2) {
+    uint16_t* kc = reinterpret_cast<uint16_t*>(p.k_cache) + tile + (int64_t)off * D + c * 8;
+    *reinterpret_cast<u32x4_t*>(kc) = kw;
+    uint16_t* vc = reinterpret_cast<uint16_t*>(p.v_cache) + tile + (int64_t)(c * 8) * BS + off;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = vw[j >> 1];
+      vc[(int64_t)j * BS] = (uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+    }
+  } else {
+    uint32_t kq[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t code = e4m3fn_encode(in_elem<IT>(kw, j) * p.k_inv_scale);
+      kq[j >> 2] |= code << (8 * (j & 3));
+    }
+    uint8_t* kc = reinterpret_cast<uint8_t*>(p.k_cache) + tile + (int64_t)off * D + c * 8;
+    *reinterpret_cast<u32x2_t*>(kc) = u32x2_t{kq[0], kq[1]};
+    uint8_t* vc = reinterpret_cast<uint8_t*>(p.v_cache) + tile + (int64_t)(c * 8) * BS + off;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      vc[(int64_t)j * BS] = (uint8_t)e4m3fn_encode(in_elem<IT>(vw, j) * p.v_inv_scale);
+    }
+  }
+}
+
+template <typename IT, typename CT, int D, int BS>
+hipError_t launch(const CacheWriteParams& p, hipStream_t stream) {
+  const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * (D / 8);
+  const int blocks = (int)((total + 255) / 256);
+  hipLaunchKernelGGL((cache_write_kernel<IT, CT, D, BS>), dim3(blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename IT, typename CT>
+hipError_t pick(const CacheWriteParams& p, int d, int bs, hipStream_t st) {
+  if (d == 64) return bs == 16 ? launch<IT, CT, 64, 16>(p, st) : launch<IT, CT, 64, 32>(p, st);
+  return bs == 16 ? launch<IT, CT, 128, 16>(p, st) : launch<IT, CT, 128, 32>(p, st);
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const CacheWriteParams& p, Dt in_dt, Dt cache_dt, int head_size,
+                              int block_size, hipStream_t stream) {
+  if (in_dt == Dt::F16) {
+    return cache_dt == Dt::FP8 ? pick<F16, FP8>(p, head_size, block_size, stream)
+                               : pick<F16, F16>(p, head_size, block_size, stream);
+  }
+  return cache_dt == Dt::FP8 ? pick<BF16, FP8>(p, head_size, block_size, stream)
+                             : pick<BF16, BF16>(p, head_size, block_size, stream);
+}
+
+}  // namespace pa

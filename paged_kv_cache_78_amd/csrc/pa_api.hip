@@ -1,0 +1,227 @@
+// C ABI of libpa: argument validation and kernel selection.  No device code
+// lives here; every check happens before anything is launched.
+#include <math.h>
+
+#include "../../include/pa.h"
+#include "pa_kernels.h"
+
+namespace {
+
+using pa::Dt;
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+bool head_size_ok(int d) { return d == 64 || d == 128; }
+bool block_size_ok(int b) { return b == 16 || b == 32; }
+bool is16(pa_dtype t) { return t == PA_F16 || t == PA_BF16; }
+Dt to_dt(pa_dtype t) { return t == PA_F16 ? Dt::F16 : (t == PA_BF16 ? Dt::BF16 : Dt::FP8); }
+bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
+
+int check_cache_types(pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale, float v_scale) {
+  if (!is16(q_dtype)) return PA_ERR_DTYPE;
+  if (cache_dtype == PA_FP8_E4M3FN) {
+    if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PA_ERR_DTYPE;
+    return PA_OK;
+  }
+  return cache_dtype == q_dtype ? PA_OK : PA_ERR_DTYPE;
+}
+
+// Shared checks of pa_decode and pa_decode_partitioned.
+int check_decode(const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_table, const int32_t* context_lens, float scale,
+                 int32_t num_kv_heads, int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                 int32_t head_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                 int64_t q_seq_stride, pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale,
+                 float v_scale) {
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens) return PA_ERR_NULL;
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (q_seq_stride < (int64_t)num_heads * head_size) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (num_seqs > 65535) return PA_ERR_SHAPE;   // grid dimension y
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (!head_size_ok(head_size) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  const int ct = check_cache_types(q_dtype, cache_dtype, k_scale, v_scale);
+  if (ct != PA_OK) return ct;
+  return PA_OK;
+}
+
+pa::DecodeParams make_params(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* context_lens,
+                             float scale, int32_t num_kv_heads, int32_t num_seqs,
+                             int32_t num_heads, int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int64_t q_seq_stride, pa_dtype cache_dtype, float k_scale,
+                             float v_scale) {
+  pa::DecodeParams p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  const bool fp8 = cache_dtype == PA_FP8_E4M3FN;
+  p.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * kLog2eHost;
+  p.v_scale = fp8 ? v_scale : 1.0f;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.q_seq_stride = q_seq_stride;
+  p.partition_size = 0;
+  p.num_partitions = 1;
+  return p;
+}
+
+hipError_t launch_decode(const pa::DecodeParams& p, pa_dtype q_dtype, pa_dtype cache_dtype,
+                         int head_size, int block_size, bool partitioned, hipStream_t stream) {
+  return pa::launch_decode_valu(p, to_dt(q_dtype), to_dt(cache_dtype), head_size, block_size,
+                                partitioned, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case PA_ERR_UNSUPPORTED: return "head size, block size or head grouping not supported";
+    case PA_ERR_DTYPE: return "element type combination or fp8 scale not supported";
+    case PA_ERR_WORKSPACE: return "invalid partition size or workspace";
+    case PA_ERR_HIP: return "the HIP runtime refused the launch";
+    default: return "unknown status";
+  }
+}
+
+int pa_abi_version(void) { return 1; }
+
+int pa_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                   const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                   int32_t head_size, int32_t block_size, int64_t num_blocks,
+                   int64_t kv_token_stride, pa_dtype in_dtype, pa_dtype cache_dtype,
+                   float k_scale, float v_scale, void* stream) {
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (kv_token_stride < (int64_t)num_kv_heads * head_size || kv_token_stride % 8 != 0)
+    return PA_ERR_SHAPE;
+  if (!head_size_ok(head_size) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  const int ct = check_cache_types(in_dtype, cache_dtype, k_scale, v_scale);
+  if (ct != PA_OK) return ct;
+  if (num_tokens == 0) return PA_OK;
+  pa::CacheWriteParams p{};
+  p.k = k;
+  p.v = v;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.kv_token_stride = kv_token_stride;
+  const bool fp8 = cache_dtype == PA_FP8_E4M3FN;
+  p.k_inv_scale = fp8 ? 1.0f / k_scale : 1.0f;
+  p.v_inv_scale = fp8 ? 1.0f / v_scale : 1.0f;
+  const hipError_t e = pa::launch_cache_write(p, to_dt(in_dtype), to_dt(cache_dtype), head_size,
+                                              block_size, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, const int32_t* context_lens, float scale,
+              int32_t num_kv_heads, int32_t block_size, int32_t num_seqs, int32_t num_heads,
+              int32_t head_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+              int64_t q_seq_stride, pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale,
+              float v_scale, void* stream) {
+  if (!out) return PA_ERR_NULL;
+  const int st = check_decode(q, k_cache, v_cache, block_table, context_lens, scale,
+                              num_kv_heads, block_size, num_seqs, num_heads, head_size,
+                              max_blocks_per_seq, num_blocks, q_seq_stride, q_dtype, cache_dtype,
+                              k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  pa::DecodeParams p = make_params(q, k_cache, v_cache, block_table, context_lens, scale,
+                                   num_kv_heads, num_seqs, num_heads, max_blocks_per_seq,
+                                   num_blocks, q_seq_stride, cache_dtype, k_scale, v_scale);
+  p.out = out;
+  const hipError_t e =
+      launch_decode(p, q_dtype, cache_dtype, head_size, block_size, false, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+size_t pa_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                    int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0 ||
+      partition_size <= 0)
+    return 0;
+  const int64_t np = ((int64_t)max_context_len + partition_size - 1) / partition_size;
+  const int64_t rows = (int64_t)num_seqs * num_heads * np;
+  return (size_t)(rows * head_size * 4 + 2 * rows * 4);
+}
+
+int pa_decode_partitioned(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* context_lens, float scale,
+                          int32_t num_kv_heads, int32_t block_size, int32_t num_seqs,
+                          int32_t num_heads, int32_t head_size, int32_t max_blocks_per_seq,
+                          int64_t num_blocks, int64_t q_seq_stride, pa_dtype q_dtype,
+                          pa_dtype cache_dtype, float k_scale, float v_scale,
+                          int32_t partition_size, int32_t max_context_len, float* tmp_out,
+                          float* max_logits, float* exp_sums, void* stream) {
+  const int st = check_decode(q, k_cache, v_cache, block_table, context_lens, scale,
+                              num_kv_heads, block_size, num_seqs, num_heads, head_size,
+                              max_blocks_per_seq, num_blocks, q_seq_stride, q_dtype, cache_dtype,
+                              k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % block_size != 0 || max_context_len < 0)
+    return PA_ERR_WORKSPACE;
+  if (!tmp_out || !max_logits || !exp_sums) return PA_ERR_NULL;
+  const int64_t np = ((int64_t)max_context_len + partition_size - 1) / partition_size;
+  if (np > 65535) return PA_ERR_WORKSPACE;   // grid dimension z
+  if (num_seqs == 0 || np == 0) return PA_OK;
+  pa::DecodeParams p = make_params(q, k_cache, v_cache, block_table, context_lens, scale,
+                                   num_kv_heads, num_seqs, num_heads, max_blocks_per_seq,
+                                   num_blocks, q_seq_stride, cache_dtype, k_scale, v_scale);
+  p.tmp_out = tmp_out;
+  p.max_logits = max_logits;
+  p.exp_sums = exp_sums;
+  p.partition_size = partition_size;
+  p.num_partitions = (int32_t)np;
+  const hipError_t e =
+      launch_decode(p, q_dtype, cache_dtype, head_size, block_size, true, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_reduce(void* out, const float* tmp_out, const float* max_logits, const float* exp_sums,
+              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+              int32_t head_size, int32_t partition_size, int32_t max_num_partitions,
+              pa_dtype out_dtype, void* stream) {
+  if (!out || !context_lens) return PA_ERR_NULL;
+  if (max_num_partitions > 0 && (!tmp_out || !max_logits || !exp_sums)) return PA_ERR_NULL;
+  if (num_seqs < 0 || num_heads <= 0 || head_size <= 0) return PA_ERR_SHAPE;
+  if (num_seqs > 65535) return PA_ERR_SHAPE;
+  if (partition_size <= 0 || max_num_partitions < 0 || max_num_partitions > 16384)
+    return PA_ERR_WORKSPACE;
+  if (!head_size_ok(head_size)) return PA_ERR_UNSUPPORTED;
+  if (!is16(out_dtype)) return PA_ERR_DTYPE;
+  if (num_seqs == 0) return PA_OK;
+  pa::ReduceParams p{};
+  p.out = out;
+  p.tmp_out = tmp_out;
+  p.max_logits = max_logits;
+  p.exp_sums = exp_sums;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.partition_size = partition_size;
+  p.max_num_partitions = max_num_partitions;
+  const hipError_t e = pa::launch_reduce(p, to_dt(out_dtype), head_size, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

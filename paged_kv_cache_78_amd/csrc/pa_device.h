@@ -1,0 +1,145 @@
+// Device-side helpers shared by the gfx950 kernels of libpa: element types,
+// raw buffer loads, DPP cross-lane reductions and the base-2 exponential.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf162_t;
+typedef __attribute__((ext_vector_type(4))) float float4_t;
+typedef __attribute__((ext_vector_type(2))) float float2_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element-type tags.  kBytes is the storage size; a 16-byte lane load holds
+// 16 / kBytes elements.
+struct F16 { static constexpr int kBytes = 2; };
+struct BF16 { static constexpr int kBytes = 2; };
+struct FP8 { static constexpr int kBytes = 1; };
+
+// ---------------------------------------------------------------------------
+// Raw buffer loads.  The descriptor base is the (uniform) tile address; a
+// descriptor with num_records = 0 turns every lane's load into a zero fill
+// with no memory access, which keeps prefetch loads unconditional at the end
+// of a range.  Word 3 = 0x00020000 is the raw-buffer format for gfx9-family
+// parts (32-bit data format, no swizzle).
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+__device__ __forceinline__ u32x2_t buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// DPP lane permutes (within 16-lane rows).
+
+constexpr int dpp_quad(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+constexpr int kDppRowRor = 0x120;       // + n, n in 1..15
+constexpr int kDppRowHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N in {1, 2, 4, 8, 16}); every lane of
+// the group receives the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group size");
+  if constexpr (N == 16) {
+    x += dpp<kDppRowRor + 8>(x);
+    x += dpp<kDppRowRor + 4>(x);
+    x += dpp<kDppRowRor + 2>(x);
+    x += dpp<kDppRowRor + 1>(x);
+  } else if constexpr (N == 8) {
+    x += dpp<kDppRowHalfMirror>(x);
+    x += dpp<dpp_quad(3, 2, 1, 0)>(x);
+    x += dpp<dpp_quad(1, 0, 3, 2)>(x);
+  } else if constexpr (N == 4) {
+    x += dpp<dpp_quad(2, 3, 0, 1)>(x);
+    x += dpp<dpp_quad(1, 0, 3, 2)>(x);
+  } else if constexpr (N == 2) {
+    x += dpp<dpp_quad(1, 0, 3, 2)>(x);
+  }
+  return x;
+}
+
+// Value of lane (lane ^ M) for M in {1, 2} (quad permutes).
+template <int M>
+__device__ __forceinline__ float xor_lane(float x) {
+  static_assert(M == 1 || M == 2, "xor distance");
+  if constexpr (M == 1) return dpp<dpp_quad(1, 0, 3, 2)>(x);
+  else return dpp<dpp_quad(2, 3, 0, 1)>(x);
+}
+
+// ---------------------------------------------------------------------------
+// Arithmetic helpers.
+
+// Reinterpret one 32-bit word as a pair of 16-bit floats.  The word is taken
+// as a scalar parameter: bit-casting an ext-vector element expression
+// (v[i]) in place does not select element i with this compiler.
+__device__ __forceinline__ half2_t as_half2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+__device__ __forceinline__ bf162_t as_bf162(uint32_t w) { return __builtin_bit_cast(bf162_t, w); }
+
+// 2^x with the hardware transcendental (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(half2_t, w)[0];
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(half2_t, w)[1];
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
+
+// Two e4m3fn codes (bytes 0,1 or 2,3 of w) -> two floats, with the gfx950
+// conversion instruction (OCP e4m3fn on this target).
+template <bool HI>
+__device__ __forceinline__ float2_t fp8x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+// Round-to-nearest-even float -> 16-bit storage.
+__device__ __forceinline__ uint16_t to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ uint16_t to_bits16(float x);
+template <>
+__device__ __forceinline__ uint16_t to_bits16<F16>(float x) { return to_f16_bits(x); }
+template <>
+__device__ __forceinline__ uint16_t to_bits16<BF16>(float x) { return to_bf16_bits(x); }
+
+}  // namespace pa

@@ -1,0 +1,71 @@
+// Internal host-side interface between the C ABI shim and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum class Dt : int { F16 = 0, BF16 = 1, FP8 = 2 };
+
+// Arguments of the decode kernels (both the one-pass and the partitioned
+// form).  Pointers are device pointers; strides are in elements.
+struct DecodeParams {
+  void* out;                 // [S, H, D] q dtype           (one pass)
+  const void* q;             // [S, H, D] row stride q_seq_stride
+  const void* k_cache;       // [NB, KVH, BS, D]
+  const void* v_cache;       // [NB, KVH, D, BS]
+  const int32_t* block_table;   // [S, MB]
+  const int32_t* context_lens;  // [S]
+  float* tmp_out;            // [S, H, NP, D]               (partitioned)
+  float* max_logits;         // [S, H, NP]
+  float* exp_sums;           // [S, H, NP]
+  float qk_scale_log2;       // scale * k_scale * log2(e)
+  float v_scale;             // 1 for 16-bit caches
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int64_t num_blocks;
+  int64_t q_seq_stride;
+  int32_t partition_size;    // tokens per partition (partitioned), else 0
+  int32_t num_partitions;    // NP (partitioned), else 1
+};
+
+struct ReduceParams {
+  void* out;
+  const float* tmp_out;
+  const float* max_logits;
+  const float* exp_sums;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t partition_size;
+  int32_t max_num_partitions;
+};
+
+struct CacheWriteParams {
+  const void* k;
+  const void* v;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int64_t num_blocks;
+  int64_t kv_token_stride;
+  float k_inv_scale;   // fp32(1 / k_scale), fp8 caches only
+  float v_inv_scale;
+};
+
+// Each returns hipSuccess or the launch error.  Shapes are validated by the
+// caller; the launchers only pick the instantiation.
+hipError_t launch_decode_valu(const DecodeParams& p, Dt q_dt, Dt cache_dt, int head_size,
+                              int block_size, bool partitioned, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, Dt q_dt, Dt cache_dt, int head_size,
+                              int block_size, bool partitioned, hipStream_t stream);
+hipError_t launch_reduce(const ReduceParams& p, Dt out_dt, int head_size, hipStream_t stream);
+hipError_t launch_cache_write(const CacheWriteParams& p, Dt in_dt, Dt cache_dt, int head_size,
+                              int block_size, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,53 @@
+"""Shared helpers of the GPU parity tests: run the CPU oracle on a workload
+and compare element by element."""
+import numpy as np
+import torch
+
+import oracle
+from workloads import to_numpy_bits
+
+# |gpu - oracle| <= atol + rtol * |oracle| per element (16-bit / fp8 caches)
+TOL = {"f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2), "e4m3fn": (5e-3, 1e-2)}
+
+
+def tol_of(wl):
+    return TOL[wl.cache_dtype]
+
+
+def oracle_arrays(wl):
+    return dict(q=to_numpy_bits(wl.q), k=to_numpy_bits(wl.k_cache), v=to_numpy_bits(wl.v_cache),
+                table=wl.block_table.cpu().numpy(), lens=wl.context_lens.cpu().numpy())
+
+
+def oracle_decode(wl, lens=None, seqs=None, heads=None, arrays=None):
+    a = arrays or oracle_arrays(wl)
+    L = a["lens"] if lens is None else np.asarray(lens, dtype=np.int32)
+    return oracle.paged_decode(a["q"], a["k"], a["v"], a["table"], L, wl.scale, wl.num_kv_heads,
+                               wl.block_size, wl.q_dtype, wl.cache_dtype, wl.k_scale, wl.v_scale,
+                               seqs=seqs, heads=heads)
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def assert_close(got, ref, atol, rtol, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(ref)), "oracle produced non-finite values"
+    assert np.all(np.isfinite(got)), f"{what}: GPU produced non-finite values"
+    err = np.abs(got - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {err.size} elements out of tolerance; worst at {i}: "
+            f"gpu {got[i]!r} oracle {ref[i]!r}; max abs err {err.max():.3e}, "
+            f"max rel err {(err / np.maximum(np.abs(ref), 1e-30)).max():.3e}")
+    return float(err.max())
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy()

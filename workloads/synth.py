@@ -155,8 +155,14 @@ def _assemble(name, ctx, table, num_blocks, gen, device, *, H, KVH, D, BS,
         shared_blocks=list(shared_ids))
 
 
-def _uniform_lengths(gen, S, lo, hi):
-    return torch.randint(lo, hi + 1, (S,), generator=gen, device=gen.device).cpu().tolist()
+def _uniform_lengths(gen, S, lo, hi, lengths=None):
+    drawn = torch.randint(lo, hi + 1, (S,), generator=gen, device=gen.device).cpu().tolist()
+    if lengths is None:
+        return drawn
+    # explicit lengths (tests of edge cases) replace the first len(lengths) draws
+    lengths = [int(x) for x in lengths]
+    assert len(lengths) <= S and all(0 <= x <= hi for x in lengths)
+    return lengths + drawn[len(lengths):]
 
 
 # ----------------------------------------------------------------------------
@@ -176,12 +182,12 @@ def worked_example(seed: int = 0, device: str = "cpu") -> Workload:
 
 def llama7b_mha(seed: int = 1, device: str = "cpu", num_seqs: int = 64,
                 len_range=(128, 2048), num_heads: int = 32, head_size: int = 128,
-                block_size: int = 16, dtype: str = "f16") -> Workload:
+                block_size: int = 16, dtype: str = "f16", lengths=None) -> Workload:
     """Llama-7B-shaped MHA decode layer: 64 sequences, 32 heads = 32 kv heads,
     head size 128, block size 16, context lengths uniform in [128, 2048],
     randomly permuted physical blocks, fp16 N(0,1)."""
     gen = _gen(seed, device)
-    ctx = _uniform_lengths(gen, num_seqs, *len_range)
+    ctx = _uniform_lengths(gen, num_seqs, *len_range, lengths=lengths)
     mb = -(-(len_range[1] + 1) // block_size)
     table, nb, _ = _allocate([c + 1 for c in ctx], block_size, mb, gen)
     return _assemble("llama7b_mha", ctx, table, nb, gen, device, H=num_heads,
@@ -190,11 +196,11 @@ def llama7b_mha(seed: int = 1, device: str = "cpu", num_seqs: int = 64,
 
 def gqa(seed: int = 2, device: str = "cpu", num_seqs: int = 128, len_range=(512, 4096),
         num_heads: int = 64, num_kv_heads: int = 8, head_size: int = 128,
-        block_size: int = 16, dtype: str = "bf16") -> Workload:
+        block_size: int = 16, dtype: str = "bf16", lengths=None) -> Workload:
     """GQA decode: 128 sequences, 64 query heads over 8 kv heads, head size
     128, block size 16, context lengths uniform in [512, 4096], bf16 N(0,1)."""
     gen = _gen(seed, device)
-    ctx = _uniform_lengths(gen, num_seqs, *len_range)
+    ctx = _uniform_lengths(gen, num_seqs, *len_range, lengths=lengths)
     mb = -(-(len_range[1] + 1) // block_size)
     table, nb, _ = _allocate([c + 1 for c in ctx], block_size, mb, gen)
     return _assemble("gqa", ctx, table, nb, gen, device, H=num_heads, KVH=num_kv_heads,
@@ -204,13 +210,13 @@ def gqa(seed: int = 2, device: str = "cpu", num_seqs: int = 128, len_range=(512,
 def long_context(seed: int = 3, device: str = "cpu", num_seqs: int = 8,
                  len_range=(32768, 131072), num_heads: int = 32, head_size: int = 128,
                  block_size: int = 16, partition_size: int = 512,
-                 dtype: str = "f16") -> Workload:
+                 dtype: str = "f16", lengths=None) -> Workload:
     """Long-context partitioned decode: 8 sequences, 32 heads = 32 kv heads,
     head size 128, block size 16, context lengths uniform in [32768, 131072],
     fp16 N(0,1), 512-token partitions.  The full-size pool is ~10.7 GB: draw
     it with device="cuda"."""
     gen = _gen(seed, device)
-    ctx = _uniform_lengths(gen, num_seqs, *len_range)
+    ctx = _uniform_lengths(gen, num_seqs, *len_range, lengths=lengths)
     mb = -(-(len_range[1] + 1) // block_size)
     table, nb, _ = _allocate([c + 1 for c in ctx], block_size, mb, gen)
     return _assemble("long_context", ctx, table, nb, gen, device, H=num_heads,
