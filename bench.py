@@ -1,0 +1,240 @@
+"""Benchmark of one decode step of paged attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one pass of the hot path over one synthetic batch that is already
+resident in HBM: pa_cache_write of every sequence's new token, then decode
+attention over context_len + 1 tokens (pa_decode, or pa_decode_partitioned +
+pa_reduce for the long-context workload).  Prints one JSON line.
+
+value = KV tokens attended per second over the K timed steps (whole job).
+roofline = the decode kernel's algorithmic HBM bytes per launch / its mean
+launch time (HIP events on the launch stream), against 8 TB/s.
+cpu_baseline = the CPU oracle (test infrastructure, fp64 numpy) on a bounded
+sample of the same workload, timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "decode attention KV tokens/s and achieved HBM GB/s (% of peak), 1×MI355X"
+ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3fn": 1}
+CSRC = os.path.join(ROOT, "paged_kv_cache_78_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl, lens) -> int:
+    """K+V of every attended token, q in, out, block-table ids, context_lens."""
+    S, H, D, KVH, BS = wl.num_seqs, wl.num_heads, wl.head_size, wl.num_kv_heads, wl.block_size
+    e_kv, e_q = ELEM_BYTES[wl.cache_dtype], ELEM_BYTES[wl.q_dtype]
+    tok = sum(lens)
+    ids = sum(-(-L // BS) for L in lens)
+    return tok * KVH * D * 2 * e_kv + 2 * S * H * D * e_q + 4 * ids + 4 * S
+
+
+def recorded_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_workload(name: str, device: str):
+    import workloads
+    if name == "long_context":
+        return workloads.long_context(device=device)        # ~10.7 GB pool: draw on the GPU
+    return workloads.make(name).to(device)
+
+
+def cpu_baseline(wl, lens, budget_s: float = 10.0):
+    """Time the CPU oracle on whole sequences of the workload (host copies of
+    just those sequences' blocks) until about budget_s has been spent."""
+    import numpy as np
+    import torch
+    import oracle
+    from workloads import to_numpy_bits
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = torch.get_num_threads()
+    S = wl.num_seqs
+    order = list(range(S))
+    done_tokens = 0
+    done_seqs = 0
+    t_total = 0.0
+    table = wl.block_table.cpu().numpy()
+    qn = to_numpy_bits(wl.q)
+    i = 0
+    while t_total < budget_s and i < 4 * S:
+        s = order[i % S]
+        i += 1
+        L = int(lens[s])
+        nblk = -(-L // wl.block_size)
+        ids = torch.from_numpy(table[s, :nblk].astype(np.int64)).to(wl.k_cache.device)
+        k = to_numpy_bits(wl.k_cache.index_select(0, ids))
+        v = to_numpy_bits(wl.v_cache.index_select(0, ids))
+        row = np.arange(nblk, dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        oracle.paged_decode(qn[s:s + 1], k, v, row, np.array([L], dtype=np.int32), wl.scale,
+                            wl.num_kv_heads, wl.block_size, wl.q_dtype, wl.cache_dtype,
+                            wl.k_scale, wl.v_scale)
+        t_total += time.perf_counter() - t0
+        done_tokens += L
+        done_seqs += 1
+    return {"value": done_tokens / t_total, "unit": "KV tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done_seqs} whole sequences (all {wl.num_heads} heads, {done_tokens} "
+                      f"KV tokens) of the same workload, fp64 numpy, {t_total:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_mha",
+                    choices=["worked_example", "llama7b_mha", "gqa", "long_context",
+                             "fp8_shared_prefix"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(decode attention shards by sequence or kv head with no exchange).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_78_amd as pa
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (ROCm) and the built libpa.so")
+    pa.lib()
+    dev = "cuda:0"
+    wl = make_workload(args.workload, dev)
+    lens_step = (wl.context_lens + 1).contiguous()       # the step attends the new token too
+    lens_host = lens_step.cpu().tolist()
+    partitioned = wl.partition_size > 0
+    P = wl.partition_size
+    max_len = max(lens_host)
+    out = torch.empty_like(wl.q)
+    ws = pa.partition_workspace(wl.num_seqs, wl.num_heads, wl.head_size, max_len, P, dev) \
+        if partitioned else None
+
+    ev = []
+
+    def step(record: bool):
+        pa.cache_write(wl.new_k, wl.new_v, wl.k_cache, wl.v_cache, wl.slot_mapping,
+                       k_scale=wl.k_scale, v_scale=wl.v_scale)
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        if partitioned:
+            pa.decode_partitioned_only(wl.q, wl.k_cache, wl.v_cache, wl.block_table, lens_step,
+                                       wl.scale, P, max_len, ws, wl.k_scale, wl.v_scale)
+        else:
+            pa.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, lens_step, wl.scale,
+                      k_scale=wl.k_scale, v_scale=wl.v_scale, out=out)
+        if record:
+            e1.record()
+            ev.append((e0, e1))
+        if partitioned:
+            pa.reduce(out, ws, lens_step, P)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens = sum(lens_host)
+    value = tokens / (ms_per_step * 1e-3)
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    alg = algorithmic_bytes(wl, lens_host)
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    kernel = "pa_decode_partitioned" if partitioned else "pa_decode"
+    src_hash = kernel_source_hash()
+    traffic = recorded_traffic(kernel, args.workload, src_hash)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, lens_host, args.cpu_budget)
+
+    kv_dt = {"f16": "f16", "bf16": "bf16", "e4m3fn": "e4m3fn KV / bf16 q"}[wl.cache_dtype]
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.q_dtype if wl.cache_dtype != "e4m3fn" else "e4m3fn",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": wl.num_seqs, "num_heads": wl.num_heads,
+            "num_kv_heads": wl.num_kv_heads, "head_size": wl.head_size,
+            "block_size": wl.block_size, "kv_dtype": kv_dt,
+            "context_tokens_per_step": tokens,
+            "partition_size": P if partitioned else None,
+            "step": "pa_cache_write + " + ("pa_decode_partitioned + pa_reduce" if partitioned
+                                           else "pa_decode"),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel,
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg,
+            "kernel_ms": kern_ms,
+            "kernel_sources": src_hash,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

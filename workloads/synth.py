@@ -106,7 +106,7 @@ def _allocate(cover: Sequence[int], block_size: int, max_blocks: int,
     share_set = set(shared["seqs"]) if shared else set()
     private = sum(n - (n_shared if s in share_set else 0) for s, n in enumerate(need))
     num_blocks = n_shared + private + spare
-    perm = torch.randperm(num_blocks, generator=gen).tolist()
+    perm = torch.randperm(num_blocks, generator=gen, device=gen.device).tolist()
     shared_ids = perm[:n_shared]
     nxt = n_shared
     table = torch.full((S, max_blocks), -1, dtype=torch.int32)
