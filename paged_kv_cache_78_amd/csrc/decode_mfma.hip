@@ -1,0 +1,385 @@
+// Paged decode attention for grouped query heads (2 <= G <= 16 query heads per
+// kv head) on the gfx950 matrix cores.
+//
+// Method (vLLM "Paged Attention" design page, sections "QK", "Softmax",
+// "Value", "LV", "Output"; the group of query heads that share one kv head
+// is named there through num_kv_heads / kv_head_idx): per (sequence, kv head
+// [, partition]) the G query heads of the group all read the same K/V tiles,
+// so the scores and the weighted value sum are dense contractions:
+//
+//   S^T [16 tokens x 16 heads] = K [16 x D] . Q^T [D x 16]     (v_mfma 16x16x32)
+//   O^T [D x 16 heads]        += V^T [D x 16] . P^T [16 x 16]   (v_mfma 16x16x16)
+//
+// One 64-lane wavefront per (sequence, kv head[, partition]), 16-token
+// sub-tiles (a block of 32 tokens is two sub-tiles).  Operand layouts:
+//  * A = K: lane l holds token l%16 and 8 consecutive head dims; the dims of
+//    the 32-wide k-chunks are chosen so each lane's 16-byte load is one
+//    contiguous piece of the token's row.  Q^T (B) uses the same dim order.
+//  * S^T lands with lane l holding head l%16 and tokens 4(l/16)..+3: exactly
+//    the B-operand layout P^T needs for the second product, and the per-head
+//    softmax state (max, rescale factor) lives in the lanes of that head's
+//    output column.
+//  * A = V^T: lane l holds head dim 16j + l%16 and tokens 4(l/16)..+3, an
+//    8-byte piece of the dim-major V tile row (4 bytes for fp8).
+//  * P is rounded to the 16-bit operand type; the softmax sum adds the same
+//    rounded weights, so weights and normaliser agree.
+//  * fp8 e4m3fn K/V convert exactly to bf16/f16 before the products; the
+//    cache scales multiply the logits (k_scale) and the output (v_scale).
+//  * The per-head max over a sub-tile's 16 tokens needs two cross-row
+//    exchanges; everything else stays in registers.  Tokens past the context
+//    get -inf logits and zeroed V operands (a NaN in an unused slot must not
+//    reach the matrix product).
+// The block table, prefetch pipeline and error handling follow the
+// one-head-per-kv-head kernel.
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) _Float16 half8_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 half4_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8v_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// 16-bit operand type of the matrix products
+template <typename QT>
+struct Mma;
+
+template <>
+struct Mma<F16> {
+  static __device__ __forceinline__ float4_t qk(u32x4_t a, u32x4_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float4_t pv(u32x2_t a, u32x2_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
+                                                 __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
+  }
+  // two floats -> packed 16-bit pair (round to nearest even)
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    return (uint32_t)to_f16_bits(lo) | ((uint32_t)to_f16_bits(hi) << 16);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) { return f16_lo(w); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return f16_hi(w); }
+  // two exactly representable floats (decoded fp8) -> packed pair
+  static __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+};
+
+template <>
+struct Mma<BF16> {
+  static __device__ __forceinline__ float4_t qk(u32x4_t a, u32x4_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v_t, a),
+                                                   __builtin_bit_cast(bf16x8v_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float4_t pv(u32x2_t a, u32x2_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    return (uint32_t)to_bf16_bits(lo) | ((uint32_t)to_bf16_bits(hi) << 16);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
+  static __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+    // upper halves of the two binary32 patterns (exact for decoded e4m3fn)
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
+                                 0x07060302u);
+  }
+};
+
+// Head dim of element e (0..7) of k-chunk c for lane group g in the QK
+// product; 16-bit caches read 16 contiguous bytes per chunk, fp8 caches read
+// 16 bytes (16 dims) that serve two consecutive chunks.
+template <int ESZ>
+__device__ __forceinline__ int qk_dim(int c, int g) {
+  if constexpr (ESZ == 2) return 32 * c + 8 * g;
+  else return 64 * (c >> 1) + 16 * g + 8 * (c & 1);
+}
+
+template <typename QT, typename CT, int D, int BS, bool PART>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
+  constexpr int ESZ = CT::kBytes;
+  constexpr int SUB = BS / 16;              // 16-token sub-tiles per block
+  constexpr int TILE_BYTES = BS * D * ESZ;
+  constexpr int NQK = D / 32;               // QK products per sub-tile
+  constexpr int NPV = D / 16;               // PV products per sub-tile
+  constexpr int NKL = ESZ == 2 ? NQK : NQK / 2;   // 16-byte K loads per sub-tile
+  constexpr int NBUF = 3;
+  static_assert(BS % 16 == 0 && D % 64 == 0, "shape");
+  using M = Mma<QT>;
+
+  const int lane = threadIdx.x;
+  const int n = lane & 15;          // head column / token row of the products
+  const int g = lane >> 4;          // lane group: k-block / row block
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
+  const int part = PART ? (int)blockIdx.z : 0;
+  const int H = p.num_heads;
+  const int KVH = p.num_kv_heads;
+  const int G = H / KVH;
+  const int L = p.context_lens[s];
+  const int MB = p.max_blocks_per_seq;
+
+  const int tiles_per_part = PART ? p.partition_size / BS : 0;
+  const int seq_tiles = (L + BS - 1) / BS;
+  const int tile0 = PART ? part * tiles_per_part : 0;
+  if (PART && L > 0 && tile0 >= seq_tiles) return;
+  const int ntiles = PART ? min(seq_tiles - tile0, tiles_per_part) : seq_tiles;
+  const bool bad_len = (L < 0) || (L > MB * BS);
+  const bool head_ok = n < G;
+  const int h = kvh * G + n;
+  const int64_t prow = (int64_t)(s * H + h) * (PART ? p.num_partitions : 1) + part;
+
+  auto write_out = [&](const float4_t (&o)[NPV]) {
+    if (!head_ok) return;
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) {
+      const int d = 16 * j + 4 * g;
+      if constexpr (PART) {
+        *reinterpret_cast<float4_t*>(p.tmp_out + prow * D + d) = o[j];
+      } else {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + (int64_t)(s * H + h) * D + d;
+        const uint32_t w0 = (uint32_t)to_bits16<QT>(o[j][0]) | ((uint32_t)to_bits16<QT>(o[j][1]) << 16);
+        const uint32_t w1 = (uint32_t)to_bits16<QT>(o[j][2]) | ((uint32_t)to_bits16<QT>(o[j][3]) << 16);
+        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w0, w1};
+      }
+    }
+  };
+
+  if (bad_len || (PART && L <= 0)) {
+    if (bad_len) {
+      float4_t o[NPV];
+      const float nanv = __builtin_nanf("");
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) o[j] = float4_t{nanv, nanv, nanv, nanv};
+      write_out(o);
+      if (PART && head_ok && g == 0) {
+        p.max_logits[prow] = nanv;
+        p.exp_sums[prow] = nanv;
+      }
+    }
+    return;
+  }
+
+  // Q^T operand: head n of the group, dims in the QK chunk order
+  u32x4_t qb[NQK];
+  {
+    const char* qrow = reinterpret_cast<const char*>(p.q) +
+                       ((int64_t)s * p.q_seq_stride + (int64_t)h * D) * 2;
+#pragma unroll
+    for (int c = 0; c < NQK; ++c) {
+      qb[c] = head_ok ? *reinterpret_cast<const u32x4_t*>(qrow + qk_dim<ESZ>(c, g) * 2)
+                      : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)kvh * TILE_BYTES;
+  const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE_BYTES;
+  const int64_t block_stride = (int64_t)KVH * TILE_BYTES;
+  const int32_t* trow = p.block_table + (int64_t)s * MB + tile0;
+
+  auto load_tbl = [&](int first) -> int {
+    const int j = first + lane;
+    return (j < ntiles) ? trow[j] : 0;
+  };
+  bool bad_id = false;
+  auto sanitize = [&](int first, int raw) -> int {
+    const bool inrange = (first + lane) < ntiles;
+    const bool bad = inrange && (raw < 0 || (int64_t)raw >= p.num_blocks);
+    bad_id |= __builtin_amdgcn_ballot_w64(bad) != 0;
+    return bad ? 0 : raw;
+  };
+  int cbase = 0;
+  int tbl_cur = sanitize(0, load_tbl(0));
+  int tbl_nxt = load_tbl(64);
+
+  // per-lane byte offsets inside a tile
+  uint32_t koff[SUB][NKL];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u)
+#pragma unroll
+    for (int i = 0; i < NKL; ++i)
+      koff[u][i] = (uint32_t)((16 * u + n) * D * ESZ +
+                              (ESZ == 2 ? qk_dim<2>(i, g) * 2 : 64 * i + 16 * g));
+  auto voff = [&](int u, int j) -> uint32_t {
+    return (uint32_t)((16 * j + n) * BS * ESZ + (16 * u + 4 * g) * ESZ);
+  };
+
+  using VReg = typename std::conditional<ESZ == 2, u32x2_t, uint32_t>::type;
+  u32x4_t kb[NBUF][SUB][NKL];
+  VReg vb[NBUF][SUB][NPV];
+
+  auto issue = [&](u32x4_t (&kd)[SUB][NKL], VReg (&vd)[SUB][NPV], int t) {
+    int phys = 0;
+    uint32_t bytes = 0;
+    if (t < ntiles) {
+      if (t - cbase == 64) {
+        cbase += 64;
+        tbl_cur = sanitize(cbase, tbl_nxt);
+        tbl_nxt = load_tbl(cbase + 64);
+      }
+      phys = __builtin_amdgcn_readlane(tbl_cur, t - cbase);
+      bytes = TILE_BYTES;
+    }
+    const int64_t off = (int64_t)phys * block_stride;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, bytes);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) kd[u][i] = buffer_load16(rk, koff[u][i]);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) {
+        if constexpr (ESZ == 2) vd[u][j] = buffer_load8(rv, voff(u, j));
+        else vd[u][j] = buffer_load4(rv, voff(u, j));
+      }
+  };
+
+  float m = kNegInf;      // running max of head n (base 2), same in all 4 lane groups
+  float l = 0.0f;         // partial sum over this lane group's tokens
+  float4_t acc[NPV];
+#pragma unroll
+  for (int j = 0; j < NPV; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const int last_len = L - (tile0 + ntiles - 1) * BS;
+
+  // K chunk c of a sub-tile as the 16-bit A operand
+  auto k_operand = [&](const u32x4_t (&kd)[NKL], int c) -> u32x4_t {
+    if constexpr (ESZ == 2) {
+      return kd[c];
+    } else {
+      const u32x4_t w = kd[c >> 1];
+      const uint32_t a = (c & 1) ? w[2] : w[0];
+      const uint32_t b = (c & 1) ? w[3] : w[1];
+      const float2_t a0 = fp8x2_to_f32<false>(a), a1 = fp8x2_to_f32<true>(a);
+      const float2_t b0 = fp8x2_to_f32<false>(b), b1 = fp8x2_to_f32<true>(b);
+      return u32x4_t{M::pack_exact(a0[0], a0[1]), M::pack_exact(a1[0], a1[1]),
+                     M::pack_exact(b0[0], b0[1]), M::pack_exact(b1[0], b1[1])};
+    }
+  };
+  auto v_operand = [&](const VReg& v) -> u32x2_t {
+    if constexpr (ESZ == 2) {
+      return v;
+    } else {
+      const float2_t v0 = fp8x2_to_f32<false>(v), v1 = fp8x2_to_f32<true>(v);
+      return u32x2_t{M::pack_exact(v0[0], v0[1]), M::pack_exact(v1[0], v1[1])};
+    }
+  };
+
+  auto process = [&](const u32x4_t (&kd)[SUB][NKL], const VReg (&vd)[SUB][NPV], bool masked) {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      float4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NQK; ++c) sc = M::qk(k_operand(kd[u], c), qb[c], sc);
+      float x[4];
+      bool ok[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = sc[r] * p.qk_scale_log2;
+        ok[r] = !masked || (16 * u + 4 * g + r) < last_len;
+        x[r] = ok[r] ? x[r] : kNegInf;
+      }
+      float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = fmaxf(m, mt);
+      const float alpha = (m == mn) ? 1.0f : exp2_hw(m - mn);
+      m = mn;
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = ok[r] ? exp2_hw(x[r] - mn) : 0.0f;
+      const uint32_t p01 = M::pack(pr[0], pr[1]);
+      const uint32_t p23 = M::pack(pr[2], pr[3]);
+      l = l * alpha + ((M::lo(p01) + M::hi(p01)) + (M::lo(p23) + M::hi(p23)));
+      const u32x2_t pb = {p01, p23};
+      uint32_t keep0 = 0xFFFFFFFFu, keep1 = 0xFFFFFFFFu;
+      if (masked) {
+        keep0 = (ok[0] ? 0x0000FFFFu : 0u) | (ok[1] ? 0xFFFF0000u : 0u);
+        keep1 = (ok[2] ? 0x0000FFFFu : 0u) | (ok[3] ? 0xFFFF0000u : 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) {
+        acc[j] *= alpha;
+        u32x2_t a = v_operand(vd[u][j]);
+        if (masked) a = u32x2_t{a[0] & keep0, a[1] & keep1};
+        acc[j] = M::pv(a, pb, acc[j]);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u) issue(kb[u], vb[u], u);
+
+  for (int t0 = 0; t0 < ntiles; t0 += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int t = t0 + u;
+      issue(kb[(u + NBUF - 1) % NBUF], vb[(u + NBUF - 1) % NBUF], t + NBUF - 1);
+      if (t < ntiles) process(kb[u], vb[u], (t == ntiles - 1) && (last_len < BS));
+    }
+  }
+
+  // the normaliser of head n: sum over the four lane groups
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+
+  float4_t o[NPV];
+  const float nanv = __builtin_nanf("");
+#pragma unroll
+  for (int j = 0; j < NPV; ++j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      o[j][r] = bad_id ? nanv : (ntiles <= 0 ? 0.0f : (acc[j][r] / l) * p.v_scale);
+    }
+  }
+  write_out(o);
+  if constexpr (PART) {
+    if (head_ok && g == 0) {
+      p.max_logits[prow] = bad_id ? nanv : m * kLn2;
+      p.exp_sums[prow] = bad_id ? nanv : l;
+    }
+  }
+}
+
+template <typename QT, typename CT, int D, int BS, bool PART>
+hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
+  dim3 grid(p.num_kv_heads, p.num_seqs, PART ? p.num_partitions : 1);
+  hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, D, BS, PART>), grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename QT, typename CT, int D, int BS>
+hipError_t pick_part(const DecodeParams& p, bool part, hipStream_t st) {
+  return part ? launch_one<QT, CT, D, BS, true>(p, st) : launch_one<QT, CT, D, BS, false>(p, st);
+}
+template <typename QT, typename CT, int D>
+hipError_t pick_bs(const DecodeParams& p, int bs, bool part, hipStream_t st) {
+  return bs == 16 ? pick_part<QT, CT, D, 16>(p, part, st) : pick_part<QT, CT, D, 32>(p, part, st);
+}
+template <typename QT, typename CT>
+hipError_t pick_d(const DecodeParams& p, int d, int bs, bool part, hipStream_t st) {
+  return d == 64 ? pick_bs<QT, CT, 64>(p, bs, part, st) : pick_bs<QT, CT, 128>(p, bs, part, st);
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeParams& p, Dt q_dt, Dt cache_dt, int head_size,
+                              int block_size, bool partitioned, hipStream_t stream) {
+  if (q_dt == Dt::F16) {
+    return cache_dt == Dt::FP8 ? pick_d<F16, FP8>(p, head_size, block_size, partitioned, stream)
+                               : pick_d<F16, F16>(p, head_size, block_size, partitioned, stream);
+  }
+  return cache_dt == Dt::FP8 ? pick_d<BF16, FP8>(p, head_size, block_size, partitioned, stream)
+                             : pick_d<BF16, BF16>(p, head_size, block_size, partitioned, stream);
+}
+
+}  // namespace pa

@@ -75,9 +75,15 @@ pa::DecodeParams make_params(const void* q, const void* k_cache, const void* v_c
   return p;
 }
 
+// One query head per kv head: vector-ALU kernel.  Grouped heads (G >= 2):
+// matrix-core kernel, one wavefront per group.
 hipError_t launch_decode(const pa::DecodeParams& p, pa_dtype q_dtype, pa_dtype cache_dtype,
                          int head_size, int block_size, bool partitioned, hipStream_t stream) {
-  return pa::launch_decode_valu(p, to_dt(q_dtype), to_dt(cache_dtype), head_size, block_size,
+  if (p.num_heads == p.num_kv_heads) {
+    return pa::launch_decode_valu(p, to_dt(q_dtype), to_dt(cache_dtype), head_size, block_size,
+                                  partitioned, stream);
+  }
+  return pa::launch_decode_mfma(p, to_dt(q_dtype), to_dt(cache_dtype), head_size, block_size,
                                 partitioned, stream);
 }
 

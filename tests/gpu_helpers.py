@@ -51,3 +51,35 @@ def assert_close(got, ref, atol, rtol, what=""):
 
 def bits16(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.int16).numpy()
+
+
+def sampled_oracle(wl, pairs, lens=None):
+    """Oracle outputs out[s, h, :] for the listed (s, h) pairs, reading only
+    the blocks of those sequences and the needed kv head (host copies)."""
+    import torch as _t
+    table = wl.block_table.cpu().numpy()
+    L = (wl.context_lens if lens is None else lens).cpu().numpy()
+    G = wl.num_heads // wl.num_kv_heads
+    res = []
+    for s, h in pairs:
+        n = oracle.num_logical_blocks(int(L[s]), wl.block_size)
+        ids = _t.from_numpy(table[s, :n].astype(np.int64)).to(wl.k_cache.device)
+        kvh = h // G
+        k = to_numpy_bits(wl.k_cache.index_select(0, ids)[:, kvh:kvh + 1])
+        v = to_numpy_bits(wl.v_cache.index_select(0, ids)[:, kvh:kvh + 1])
+        q = to_numpy_bits(wl.q[s:s + 1, h:h + 1])
+        row = np.arange(max(n, 1), dtype=np.int32)[None, :]
+        out = oracle.paged_decode(q, k, v, row, np.array([L[s]], dtype=np.int32), wl.scale, 1,
+                                  wl.block_size, wl.q_dtype, wl.cache_dtype, wl.k_scale,
+                                  wl.v_scale)
+        res.append(out[0, 0])
+    return np.stack(res)
+
+
+def sample_pairs(wl, count, seed=0):
+    """(s, h) pairs: the longest and shortest sequences plus random ones."""
+    rng = np.random.default_rng(seed)
+    L = wl.context_lens.cpu().numpy()
+    seqs = [int(np.argmax(L)), int(np.argmin(L))]
+    seqs += [int(x) for x in rng.integers(0, wl.num_seqs, count - 2)]
+    return [(s, int(rng.integers(0, wl.num_heads))) for s in seqs]
