@@ -33,8 +33,12 @@
 // one-head-per-kv-head kernel.
 #include <type_traits>
 
-#include "pa_device.h"
+#include "pa_decode_common.h"
 #include "pa_kernels.h"
+
+#ifndef PA_MFMA_NBUF
+#define PA_MFMA_NBUF 3
+#endif
 
 namespace pa {
 namespace {
@@ -83,7 +87,10 @@ struct Mma<BF16> {
                                                      __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    return (uint32_t)to_bf16_bits(lo) | ((uint32_t)to_bf16_bits(hi) << 16);
+    bf162_t r;
+    r[0] = (__bf16)lo;   // v_cvt_pk_bf16_f32: round to nearest even
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
   }
   static __device__ __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
   static __device__ __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
@@ -111,18 +118,28 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int NQK = D / 32;               // QK products per sub-tile
   constexpr int NPV = D / 16;               // PV products per sub-tile
   constexpr int NKL = ESZ == 2 ? NQK : NQK / 2;   // 16-byte K loads per sub-tile
-  constexpr int NBUF = 3;
+  constexpr int NBUF = PA_MFMA_NBUF;
   static_assert(BS % 16 == 0 && D % 64 == 0, "shape");
   using M = Mma<QT>;
 
+  __shared__ int s_hist[PART ? 1 : kSchedKeys];
   const int lane = threadIdx.x;
   const int n = lane & 15;          // head column / token row of the products
   const int g = lane >> 4;          // lane group: k-block / row block
-  const int kvh = blockIdx.x;
-  const int s = blockIdx.y;
-  const int part = PART ? (int)blockIdx.z : 0;
   const int H = p.num_heads;
   const int KVH = p.num_kv_heads;
+  int kvh, s, part;
+  if constexpr (PART) {
+    kvh = blockIdx.x;
+    s = blockIdx.y;
+    part = blockIdx.z;
+  } else {
+    const int rank = (int)blockIdx.x / KVH;
+    kvh = (int)blockIdx.x % KVH;
+    s = p.order_by_length ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist, lane)
+                          : rank;
+    part = 0;
+  }
   const int G = H / KVH;
   const int L = p.context_lens[s];
   const int MB = p.max_blocks_per_seq;
@@ -183,22 +200,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)kvh * TILE_BYTES;
   const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE_BYTES;
   const int64_t block_stride = (int64_t)KVH * TILE_BYTES;
-  const int32_t* trow = p.block_table + (int64_t)s * MB + tile0;
-
-  auto load_tbl = [&](int first) -> int {
-    const int j = first + lane;
-    return (j < ntiles) ? trow[j] : 0;
-  };
-  bool bad_id = false;
-  auto sanitize = [&](int first, int raw) -> int {
-    const bool inrange = (first + lane) < ntiles;
-    const bool bad = inrange && (raw < 0 || (int64_t)raw >= p.num_blocks);
-    bad_id |= __builtin_amdgcn_ballot_w64(bad) != 0;
-    return bad ? 0 : raw;
-  };
-  int cbase = 0;
-  int tbl_cur = sanitize(0, load_tbl(0));
-  int tbl_nxt = load_tbl(64);
+  TableWindow tw;
+  tw.init(p.block_table + (int64_t)s * MB + tile0, ntiles, p.num_blocks, lane);
 
   // per-lane byte offsets inside a tile
   uint32_t koff[SUB][NKL];
@@ -220,12 +223,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
     int phys = 0;
     uint32_t bytes = 0;
     if (t < ntiles) {
-      if (t - cbase == 64) {
-        cbase += 64;
-        tbl_cur = sanitize(cbase, tbl_nxt);
-        tbl_nxt = load_tbl(cbase + 64);
-      }
-      phys = __builtin_amdgcn_readlane(tbl_cur, t - cbase);
+      phys = tw.phys(t, lane);
       bytes = TILE_BYTES;
     }
     const int64_t off = (int64_t)phys * block_stride;
@@ -244,7 +242,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
       }
   };
 
-  float m = kNegInf;      // running max of head n (base 2), same in all 4 lane groups
+  // Softmax state of head n, base 2.  m is the reference the weights are
+  // taken against, the same in all four lane groups; it only moves when a
+  // logit exceeds it by more than kSlack (so weights stay <= 2^kSlack and
+  // most sub-tiles skip the cross-group max and the rescale).  mx is this
+  // lane's true running max.
+  constexpr float kSlack = 8.0f;
+  float m = kNegInf;
+  float mx = kNegInf;
   float l = 0.0f;         // partial sum over this lane group's tokens
   float4_t acc[NPV];
 #pragma unroll
@@ -289,17 +294,25 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
         x[r] = ok[r] ? x[r] : kNegInf;
       }
       float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m, mt);
-      const float alpha = (m == mn) ? 1.0f : exp2_hw(m - mn);
-      m = mn;
+      mx = fmaxf(mx, mt);
+      if (__builtin_amdgcn_ballot_w64(mt > m + kSlack) != 0) {
+        // raise each head's reference to the larger of it and this
+        // sub-tile's max (earlier logits stay within kSlack of it)
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(m, mt);
+        const float alpha = (m == mn) ? 1.0f : exp2_hw(m - mn);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) acc[j] *= alpha;
+      }
       float pr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = ok[r] ? exp2_hw(x[r] - mn) : 0.0f;
+      for (int r = 0; r < 4; ++r) pr[r] = ok[r] ? exp2_hw(x[r] - m) : 0.0f;
       const uint32_t p01 = M::pack(pr[0], pr[1]);
       const uint32_t p23 = M::pack(pr[2], pr[3]);
-      l = l * alpha + ((M::lo(p01) + M::hi(p01)) + (M::lo(p23) + M::hi(p23)));
+      l += (M::lo(p01) + M::hi(p01)) + (M::lo(p23) + M::hi(p23));
       const u32x2_t pb = {p01, p23};
       uint32_t keep0 = 0xFFFFFFFFu, keep1 = 0xFFFFFFFFu;
       if (masked) {
@@ -308,7 +321,6 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
       }
 #pragma unroll
       for (int j = 0; j < NPV; ++j) {
-        acc[j] *= alpha;
         u32x2_t a = v_operand(vd[u][j]);
         if (masked) a = u32x2_t{a[0] & keep0, a[1] & keep1};
         acc[j] = M::pv(a, pb, acc[j]);
@@ -328,9 +340,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
     }
   }
 
-  // the normaliser of head n: sum over the four lane groups
+  // the normaliser of head n: sum over the four lane groups; the partial
+  // triple reports the exact max, with the sum re-referenced to it
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
 
   float4_t o[NPV];
   const float nanv = __builtin_nanf("");
@@ -338,21 +353,22 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   for (int j = 0; j < NPV; ++j) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      o[j][r] = bad_id ? nanv : (ntiles <= 0 ? 0.0f : (acc[j][r] / l) * p.v_scale);
+      o[j][r] = tw.bad ? nanv : (ntiles <= 0 ? 0.0f : (acc[j][r] / l) * p.v_scale);
     }
   }
   write_out(o);
   if constexpr (PART) {
     if (head_ok && g == 0) {
-      p.max_logits[prow] = bad_id ? nanv : m * kLn2;
-      p.exp_sums[prow] = bad_id ? nanv : l;
+      p.max_logits[prow] = tw.bad ? nanv : mx * kLn2;
+      p.exp_sums[prow] = tw.bad ? nanv : (mx == m ? l : l * exp2_hw(m - mx));
     }
   }
 }
 
 template <typename QT, typename CT, int D, int BS, bool PART>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.num_kv_heads, p.num_seqs, PART ? p.num_partitions : 1);
+  const dim3 grid = PART ? dim3(p.num_kv_heads, p.num_seqs, p.num_partitions)
+                        : dim3(p.num_kv_heads * p.num_seqs, 1, 1);
   hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, D, BS, PART>), grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }

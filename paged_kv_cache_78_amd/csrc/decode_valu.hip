@@ -30,8 +30,12 @@
 //    broadcast per tile with v_readlane; the next 64 are loaded a chunk ahead.
 //    Ids outside [0, num_blocks) are replaced by 0 before any address is
 //    formed and make the row NaN.
-#include "pa_device.h"
+#include "pa_decode_common.h"
 #include "pa_kernels.h"
+
+#ifndef PA_VALU_NBUF
+#define PA_VALU_NBUF 3
+#endif
 
 namespace pa {
 namespace {
@@ -160,17 +164,29 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   constexpr int TPI = kWave / LPT;          // K: tokens per load instruction
   constexpr int LPR = BS / VEC;             // V: lanes per head-dim row
   constexpr int RPI = kWave / LPR;          // V: rows per load instruction
-  constexpr int NBUF = 3;                   // tiles resident: 1 in use + 2 in flight
+  constexpr int NBUF = PA_VALU_NBUF;        // tiles resident: 1 in use, the rest in flight
   static_assert(NLOAD * TPI == BS && NLOAD * RPI == D, "tile mapping");
   static_assert(LPT >= 1 && LPT <= 16 && LPR >= 1 && LPR <= 4 && NLOAD <= LPT, "lane mapping");
 
   __shared__ __attribute__((aligned(16))) float s_scores[BS];
+  __shared__ int s_hist[PART ? 1 : kSchedKeys];
 
   const int lane = threadIdx.x;
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  const int part = PART ? (int)blockIdx.z : 0;
   const int H = p.num_heads;
+  int h, s, part;
+  if constexpr (PART) {
+    h = blockIdx.x;
+    s = blockIdx.y;
+    part = blockIdx.z;
+  } else {
+    // one pass: workgroup b takes head b % H of the sequence at position
+    // b / H of the longest-first order (or of index order)
+    const int rank = (int)blockIdx.x / H;
+    h = (int)blockIdx.x % H;
+    s = p.order_by_length ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist, lane)
+                          : rank;
+    part = 0;
+  }
   const int L = p.context_lens[s];
   const int MB = p.max_blocks_per_seq;
 
@@ -223,23 +239,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)kvh * TILE_BYTES;
   const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE_BYTES;
   const int64_t block_stride = (int64_t)p.num_kv_heads * TILE_BYTES;
-  const int32_t* trow = p.block_table + (int64_t)s * MB + tile0;
-
-  // block-table window: entries [cbase, cbase + 64) in tbl_cur, next 64 in tbl_nxt
-  auto load_tbl = [&](int first) -> int {
-    const int j = first + lane;
-    return (j < ntiles) ? trow[j] : 0;
-  };
-  bool bad_id = false;
-  auto sanitize = [&](int first, int raw) -> int {
-    const bool inrange = (first + lane) < ntiles;
-    const bool bad = inrange && (raw < 0 || (int64_t)raw >= p.num_blocks);
-    bad_id |= __builtin_amdgcn_ballot_w64(bad) != 0;
-    return bad ? 0 : raw;
-  };
-  int cbase = 0;
-  int tbl_cur = sanitize(0, load_tbl(0));
-  int tbl_nxt = load_tbl(64);
+  TableWindow tw;
+  tw.init(p.block_table + (int64_t)s * MB + tile0, ntiles, p.num_blocks, lane);
 
   u32x4_t kb[NBUF][NLOAD];
   u32x4_t vb[NBUF][NLOAD];
@@ -248,12 +249,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
     int phys = 0;
     uint32_t bytes = 0;
     if (n < ntiles) {
-      if (n - cbase == 64) {
-        cbase += 64;
-        tbl_cur = sanitize(cbase, tbl_nxt);
-        tbl_nxt = load_tbl(cbase + 64);
-      }
-      phys = __builtin_amdgcn_readlane(tbl_cur, n - cbase);
+      phys = tw.phys(n, lane);
       bytes = TILE_BYTES;
     }
     const int64_t off = (int64_t)phys * block_stride;
@@ -399,7 +395,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   }
 
   float res[NLOAD];
-  if (bad_id) {
+  if (tw.bad) {
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) res[i] = __builtin_nanf("");
   } else if (ntiles <= 0) {
@@ -413,15 +409,16 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   if constexpr (PART) {
     if (lane == 0) {
       const int64_t idx = (int64_t)row * p.num_partitions + part;
-      p.max_logits[idx] = bad_id ? __builtin_nanf("") : m * kLn2;
-      p.exp_sums[idx] = bad_id ? __builtin_nanf("") : l;
+      p.max_logits[idx] = tw.bad ? __builtin_nanf("") : m * kLn2;
+      p.exp_sums[idx] = tw.bad ? __builtin_nanf("") : l;
     }
   }
 }
 
 template <typename QT, typename CT, int D, int BS, bool PART>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.num_heads, p.num_seqs, PART ? p.num_partitions : 1);
+  const dim3 grid = PART ? dim3(p.num_heads, p.num_seqs, p.num_partitions)
+                        : dim3(p.num_heads * p.num_seqs, 1, 1);
   hipLaunchKernelGGL((decode_valu_kernel<QT, CT, D, BS, PART>), grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }

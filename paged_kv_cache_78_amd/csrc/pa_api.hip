@@ -10,6 +10,7 @@ namespace {
 using pa::Dt;
 
 constexpr float kLog2eHost = 1.4426950408889634f;
+constexpr int kMaxOrderedSeqs = 1024;
 
 bool head_size_ok(int d) { return d == 64 || d == 128; }
 bool block_size_ok(int b) { return b == 16 || b == 32; }
@@ -40,7 +41,8 @@ int check_decode(const void* q, const void* k_cache, const void* v_cache,
   if (num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   if (q_seq_stride < (int64_t)num_heads * head_size) return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
-  if (num_seqs > 65535) return PA_ERR_SHAPE;   // grid dimension y
+  if (num_seqs > 65535) return PA_ERR_SHAPE;   // grid dimension y (partitioned)
+  if ((int64_t)num_seqs * num_heads > INT32_MAX) return PA_ERR_SHAPE;
   if (!isfinite(scale)) return PA_ERR_SHAPE;
   if (!head_size_ok(head_size) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
   if (num_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
@@ -72,6 +74,9 @@ pa::DecodeParams make_params(const void* q, const void* k_cache, const void* v_c
   p.q_seq_stride = q_seq_stride;
   p.partition_size = 0;
   p.num_partitions = 1;
+  // every workgroup re-derives the order from context_lens: worth it while
+  // that scan is short
+  p.order_by_length = num_seqs <= kMaxOrderedSeqs ? 1 : 0;
   return p;
 }
 

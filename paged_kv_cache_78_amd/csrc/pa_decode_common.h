@@ -1,0 +1,125 @@
+// Pieces shared by the decode kernels: the block-table window and the
+// longest-first order of sequences.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+// Block-table window of one wavefront.  Entries [cbase, cbase + 64) of the
+// range's table slice sit one per lane in `cur`, the next 64 in `nxt` (loaded
+// a chunk ahead).  Loads go through a buffer descriptor sized to the slice, so
+// lanes past the end read 0 without branches and nothing waits on the load
+// until the chunk is used.  Entries outside [0, num_blocks) are replaced by 0
+// before any address is formed and set `bad`.
+struct TableWindow {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int ntiles;
+  int64_t num_blocks;
+  int cbase;
+  int cur;
+  int nxt;
+  bool bad;
+
+  __device__ __forceinline__ int raw(int first, int lane) {
+    return (int)buffer_load4(rsrc, (uint32_t)(first + lane) * 4u);
+  }
+  __device__ __forceinline__ int sanitize(int first, int lane, int v) {
+    const bool inrange = (first + lane) < ntiles;
+    const bool b = inrange && (v < 0 || (int64_t)v >= num_blocks);
+    bad |= __builtin_amdgcn_ballot_w64(b) != 0;
+    return b ? 0 : v;
+  }
+  __device__ __forceinline__ void init(const int32_t* slice, int n, int64_t nb, int lane) {
+    rsrc = make_rsrc(slice, (uint32_t)(n > 0 ? n : 0) * 4u);
+    ntiles = n;
+    num_blocks = nb;
+    cbase = 0;
+    bad = false;
+    cur = sanitize(0, lane, raw(0, lane));
+    nxt = raw(64, lane);
+  }
+  // Physical block of tile t (wave-uniform, t < ntiles, called with t
+  // increasing by one).
+  __device__ __forceinline__ int phys(int t, int lane) {
+    if (t - cbase == 64) {
+      cbase += 64;
+      cur = sanitize(cbase, lane, nxt);
+      nxt = raw(cbase + 64, lane);
+    }
+    return __builtin_amdgcn_readlane(cur, t - cbase);
+  }
+};
+
+// Longest-first order of sequences, computed by every workgroup of a
+// one-pass launch from context_lens alone (no workspace, no host sync).
+// Workgroups are dispatched in index order and spread over the compute units,
+// so handing the longest contexts to the first workgroups evens out the work
+// each compute unit receives.  Key: number of blocks (clamped to 255),
+// descending; ties keep sequence order.  Counting sort over 256 keys in LDS,
+// one wavefront.  Returns the sequence at position `rank`.
+constexpr int kSchedKeys = 256;
+
+__device__ __forceinline__ int sched_key(int len, int block_size) {
+  const int nb = len > 0 ? (len + block_size - 1) / block_size : 0;
+  return (kSchedKeys - 1) - (nb < kSchedKeys - 1 ? nb : kSchedKeys - 1);
+}
+
+__device__ __forceinline__ int seq_by_rank(const int32_t* context_lens, int num_seqs,
+                                           int block_size, int rank, int* hist, int lane) {
+#pragma unroll
+  for (int i = 0; i < kSchedKeys / kWave; ++i) hist[lane + i * kWave] = 0;
+  __syncthreads();
+  for (int s = lane; s < num_seqs; s += kWave) atomicAdd(&hist[sched_key(context_lens[s], block_size)], 1);
+  __syncthreads();
+  // lane owns keys [4 lane, 4 lane + 4): exclusive prefix over lanes
+  int c[4];
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = hist[4 * lane + i];
+    tot += c[i];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  const int excl = incl - tot;
+  const uint64_t own = __builtin_amdgcn_ballot_w64(excl <= rank && rank < incl);
+  const int owner = own ? (int)__builtin_ctzll(own) : 0;
+  // first of this lane's keys whose range holds `rank` (empty keys skipped)
+  int key = 4 * lane + 3, start = excl;
+  bool found = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!found) {
+      if (rank < start + c[i]) {
+        key = 4 * lane + i;
+        found = true;
+      } else {
+        start += c[i];
+      }
+    }
+  }
+  key = __builtin_amdgcn_readlane(key, owner);
+  int target = rank - __builtin_amdgcn_readlane(start, owner);
+  // the target-th sequence (in index order) carrying that key
+  for (int base = 0; base < num_seqs; base += kWave) {
+    const int s = base + lane;
+    const bool match = s < num_seqs && sched_key(context_lens[s], block_size) == key;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(match);
+    const int cnt = __builtin_popcountll(m);
+    if (target < cnt) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(match && below == target);
+      return base + (int)__builtin_ctzll(hit);
+    }
+    target -= cnt;
+  }
+  return 0;   // rank >= num_seqs: not reached for valid launches
+}
+
+}  // namespace pa

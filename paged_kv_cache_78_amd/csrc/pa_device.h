@@ -129,10 +129,7 @@ __device__ __forceinline__ uint16_t to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
-  uint32_t u = __builtin_bit_cast(uint32_t, x);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)x);   // v_cvt_pk_bf16_f32 on gfx950
 }
 
 template <typename T>

@@ -30,6 +30,7 @@ struct DecodeParams {
   int64_t q_seq_stride;
   int32_t partition_size;    // tokens per partition (partitioned), else 0
   int32_t num_partitions;    // NP (partitioned), else 1
+  int32_t order_by_length;   // one pass: dispatch the longest contexts first
 };
 
 struct ReduceParams {
