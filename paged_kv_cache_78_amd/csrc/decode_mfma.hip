@@ -134,8 +134,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
     s = blockIdx.y;
     part = blockIdx.z;
   } else {
-    const int rank = (int)blockIdx.x / KVH;
-    kvh = (int)blockIdx.x % KVH;
+    const int pos = p.order_by_length
+                        ? snake_position((int)blockIdx.x, (int)gridDim.x, p.num_cus)
+                        : (int)blockIdx.x;
+    const int rank = pos / KVH;
+    kvh = pos % KVH;
     s = p.order_by_length ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist, lane)
                           : rank;
     part = 0;

@@ -181,8 +181,11 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   } else {
     // one pass: workgroup b takes head b % H of the sequence at position
     // b / H of the longest-first order (or of index order)
-    const int rank = (int)blockIdx.x / H;
-    h = (int)blockIdx.x % H;
+    const int pos = p.order_by_length
+                        ? snake_position((int)blockIdx.x, (int)gridDim.x, p.num_cus)
+                        : (int)blockIdx.x;
+    const int rank = pos / H;
+    h = pos % H;
     s = p.order_by_length ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist, lane)
                           : rank;
     part = 0;

@@ -12,6 +12,21 @@ using pa::Dt;
 constexpr float kLog2eHost = 1.4426950408889634f;
 constexpr int kMaxOrderedSeqs = 1024;
 
+// Compute units of the current device, asked once per device (256 if the
+// runtime cannot say).
+int compute_units() {
+  static int cache[64];   // 0 = not asked yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 bool head_size_ok(int d) { return d == 64 || d == 128; }
 bool block_size_ok(int b) { return b == 16 || b == 32; }
 bool is16(pa_dtype t) { return t == PA_F16 || t == PA_BF16; }
@@ -77,6 +92,7 @@ pa::DecodeParams make_params(const void* q, const void* k_cache, const void* v_c
   // every workgroup re-derives the order from context_lens: worth it while
   // that scan is short
   p.order_by_length = num_seqs <= kMaxOrderedSeqs ? 1 : 0;
+  p.num_cus = compute_units();
   return p;
 }
 

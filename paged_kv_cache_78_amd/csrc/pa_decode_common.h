@@ -122,4 +122,16 @@ __device__ __forceinline__ int seq_by_rank(const int32_t* context_lens, int num_
   return 0;   // rank >= num_seqs: not reached for valid launches
 }
 
+// Position in the longest-first list that workgroup b takes.  Workgroups go
+// to compute units round-robin, so consecutive strata of `units` workgroups
+// alternate direction (a snake): each compute unit then gets one long and
+// one short item from every pair of strata instead of always the longer one.
+__device__ __forceinline__ int snake_position(int b, int total, int units) {
+  const int k = b / units;
+  const int i = b - k * units;
+  if ((k & 1) == 0) return b;
+  const int m = min(units, total - k * units);   // size of this stratum
+  return k * units + (m - 1 - i);
+}
+
 }  // namespace pa
