@@ -127,6 +127,9 @@ def main(argv=None):
                              "fp8_shared_prefix"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="before the warm-up, run one plain device copy of BYTES bytes "
+                         "(reference dispatch for rocprofv3 FETCH_SIZE/WRITE_SIZE scaling)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -171,6 +174,12 @@ def main(argv=None):
         if partitioned:
             pa.reduce(out, ws, lens_step, P)
 
+    if args.copy_calibration > 0:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
