@@ -39,6 +39,9 @@
 #ifndef PA_MFMA_NBUF
 #define PA_MFMA_NBUF 3
 #endif
+#ifndef PA_MFMA_WAVES
+#define PA_MFMA_WAVES 4
+#endif
 
 namespace pa {
 namespace {
@@ -110,8 +113,8 @@ __device__ __forceinline__ int qk_dim(int c, int g) {
   else return 64 * (c >> 1) + 16 * g + 8 * (c & 1);
 }
 
-template <typename QT, typename CT, int D, int BS, bool PART>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
+template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int ESZ = CT::kBytes;
   constexpr int SUB = BS / 16;              // 16-token sub-tiles per block
   constexpr int TILE_BYTES = BS * D * ESZ;
@@ -122,8 +125,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   static_assert(BS % 16 == 0 && D % 64 == 0, "shape");
   using M = Mma<QT>;
 
-  __shared__ int s_hist[PART ? 1 : kSchedKeys];
-  const int lane = threadIdx.x;
+  // WAVES wavefronts share one (sequence, kv head[, partition]): wavefront w
+  // takes the w-th contiguous share of its tiles; the states merge in LDS.
+  constexpr int NSTATE = NPV * 4 + 4;       // floats of one lane's softmax state
+  __shared__ int s_hist[PART ? 1 : WAVES * kSchedKeys];
+  __shared__ float s_state[WAVES > 1 ? (WAVES - 1) * kWave * NSTATE : 1];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15;          // head column / token row of the products
   const int g = lane >> 4;          // lane group: k-block / row block
   const int H = p.num_heads;
@@ -139,8 +147,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
                         : (int)blockIdx.x;
     const int rank = pos / KVH;
     kvh = pos % KVH;
-    s = p.order_by_length ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist, lane)
-                          : rank;
+    s = p.order_by_length
+            ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist + wave * kSchedKeys, lane)
+            : rank;
     part = 0;
   }
   const int G = H / KVH;
@@ -151,7 +160,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   const int seq_tiles = (L + BS - 1) / BS;
   const int tile0 = PART ? part * tiles_per_part : 0;
   if (PART && L > 0 && tile0 >= seq_tiles) return;
-  const int ntiles = PART ? min(seq_tiles - tile0, tiles_per_part) : seq_tiles;
+  const int ntiles_all = PART ? min(seq_tiles - tile0, tiles_per_part) : seq_tiles;
+  const int share = (ntiles_all + WAVES - 1) / WAVES;
+  const int my_first = tile0 + wave * share;          // first tile of this wavefront
+  const int ntiles = max(0, min(share, ntiles_all - wave * share));
+  const int last_tile = tile0 + ntiles_all - 1;       // the only tile that can be partial
   const bool bad_len = (L < 0) || (L > MB * BS);
   const bool head_ok = n < G;
   const int h = kvh * G + n;
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   };
 
   if (bad_len || (PART && L <= 0)) {
-    if (bad_len) {
+    if (bad_len && wave == 0) {
       float4_t o[NPV];
       const float nanv = __builtin_nanf("");
 #pragma unroll
@@ -204,7 +217,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE_BYTES;
   const int64_t block_stride = (int64_t)KVH * TILE_BYTES;
   TableWindow tw;
-  tw.init(p.block_table + (int64_t)s * MB + tile0, ntiles, p.num_blocks, lane);
+  tw.init(p.block_table + (int64_t)s * MB + my_first, ntiles, p.num_blocks, lane);
 
   // per-lane byte offsets inside a tile
   uint32_t koff[SUB][NKL];
@@ -257,7 +270,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   float4_t acc[NPV];
 #pragma unroll
   for (int j = 0; j < NPV; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-  const int last_len = L - (tile0 + ntiles - 1) * BS;
+  const int last_len = L - last_tile * BS;
 
   // K chunk c of a sub-tile as the 16-bit A operand
   auto k_operand = [&](const u32x4_t (&kd)[NKL], int c) -> u32x4_t {
@@ -339,7 +352,41 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
     for (int u = 0; u < NBUF; ++u) {
       const int t = t0 + u;
       issue(kb[(u + NBUF - 1) % NBUF], vb[(u + NBUF - 1) % NBUF], t + NBUF - 1);
-      if (t < ntiles) process(kb[u], vb[u], (t == ntiles - 1) && (last_len < BS));
+      if (t < ntiles) process(kb[u], vb[u], (my_first + t == last_tile) && (last_len < BS));
+    }
+  }
+
+  bool bad = tw.bad;
+  if constexpr (WAVES > 1) {
+    // merge the wavefronts' states (each with its own reference max)
+    if (wave > 0) {
+      float* st = s_state + ((wave - 1) * kWave + lane) * NSTATE;
+#pragma unroll
+      for (int j = 0; j < NPV; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[4 * j + r] = acc[j][r];
+      st[NPV * 4 + 0] = m;
+      st[NPV * 4 + 1] = mx;
+      st[NPV * 4 + 2] = l;
+      st[NPV * 4 + 3] = bad ? 1.0f : 0.0f;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+      const float* st = s_state + ((w - 1) * kWave + lane) * NSTATE;
+      const float mo = st[NPV * 4 + 0];
+      const float mn = fmaxf(m, mo);
+      const float fa = (m == mn) ? 1.0f : exp2_hw(m - mn);
+      const float fb = (mo == mn) ? 1.0f : exp2_hw(mo - mn);
+#pragma unroll
+      for (int j = 0; j < NPV; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] = acc[j][r] * fa + st[4 * j + r] * fb;
+      l = l * fa + st[NPV * 4 + 2] * fb;
+      mx = fmaxf(mx, st[NPV * 4 + 1]);
+      bad |= st[NPV * 4 + 3] != 0.0f;
+      m = mn;
     }
   }
 
@@ -356,29 +403,33 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   for (int j = 0; j < NPV; ++j) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      o[j][r] = tw.bad ? nanv : (ntiles <= 0 ? 0.0f : (acc[j][r] / l) * p.v_scale);
+      o[j][r] = bad ? nanv : (ntiles_all <= 0 ? 0.0f : (acc[j][r] / l) * p.v_scale);
     }
   }
   write_out(o);
   if constexpr (PART) {
     if (head_ok && g == 0) {
-      p.max_logits[prow] = tw.bad ? nanv : mx * kLn2;
-      p.exp_sums[prow] = tw.bad ? nanv : (mx == m ? l : l * exp2_hw(m - mx));
+      p.max_logits[prow] = bad ? nanv : mx * kLn2;
+      p.exp_sums[prow] = bad ? nanv : (mx == m ? l : l * exp2_hw(m - mx));
     }
   }
 }
 
-template <typename QT, typename CT, int D, int BS, bool PART>
+template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid = PART ? dim3(p.num_kv_heads, p.num_seqs, p.num_partitions)
                         : dim3(p.num_kv_heads * p.num_seqs, 1, 1);
-  hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, D, BS, PART>), grid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, D, BS, PART, WAVES>), grid, dim3(64 * WAVES), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
+// Partitions already give every wavefront a bounded share: one wavefront per
+// workgroup.  One pass: PA_MFMA_WAVES wavefronts split each sequence.
 template <typename QT, typename CT, int D, int BS>
 hipError_t pick_part(const DecodeParams& p, bool part, hipStream_t st) {
-  return part ? launch_one<QT, CT, D, BS, true>(p, st) : launch_one<QT, CT, D, BS, false>(p, st);
+  return part ? launch_one<QT, CT, D, BS, true, 1>(p, st)
+              : launch_one<QT, CT, D, BS, false, PA_MFMA_WAVES>(p, st);
 }
 template <typename QT, typename CT, int D>
 hipError_t pick_bs(const DecodeParams& p, int bs, bool part, hipStream_t st) {

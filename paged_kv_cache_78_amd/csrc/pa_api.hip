@@ -11,6 +11,8 @@ using pa::Dt;
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 constexpr int kMaxOrderedSeqs = 1024;
+// pa_reduce keeps one fp32 weight per partition in LDS (60 KiB at most)
+constexpr int kMaxPartitions = 15360;
 
 // Compute units of the current device, asked once per device (256 if the
 // runtime cannot say).
@@ -232,7 +234,7 @@ int pa_reduce(void* out, const float* tmp_out, const float* max_logits, const fl
   if (max_num_partitions > 0 && (!tmp_out || !max_logits || !exp_sums)) return PA_ERR_NULL;
   if (num_seqs < 0 || num_heads <= 0 || head_size <= 0) return PA_ERR_SHAPE;
   if (num_seqs > 65535) return PA_ERR_SHAPE;
-  if (partition_size <= 0 || max_num_partitions < 0 || max_num_partitions > 16384)
+  if (partition_size <= 0 || max_num_partitions < 0 || max_num_partitions > kMaxPartitions)
     return PA_ERR_WORKSPACE;
   if (!head_size_ok(head_size)) return PA_ERR_UNSUPPORTED;
   if (!is16(out_dtype)) return PA_ERR_DTYPE;
