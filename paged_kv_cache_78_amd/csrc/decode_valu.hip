@@ -36,6 +36,9 @@
 #ifndef PA_VALU_NBUF
 #define PA_VALU_NBUF 3
 #endif
+#ifndef PA_VALU_WAVES
+#define PA_VALU_WAVES 4
+#endif
 
 namespace pa {
 namespace {
@@ -154,8 +157,8 @@ __device__ __forceinline__ void v_decode(const u32x4_t& v, float (&out)[16 / CT:
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-template <typename QT, typename CT, int D, int BS, bool PART>
-__global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
+template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodeParams p) {
   constexpr int ESZ = CT::kBytes;
   constexpr int VEC = 16 / ESZ;             // cache elements per 16-byte lane load
   constexpr int TILE_BYTES = BS * D * ESZ;  // one (block, kv head) tile of K or of V
@@ -168,10 +171,16 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   static_assert(NLOAD * TPI == BS && NLOAD * RPI == D, "tile mapping");
   static_assert(LPT >= 1 && LPT <= 16 && LPR >= 1 && LPR <= 4 && NLOAD <= LPT, "lane mapping");
 
-  __shared__ __attribute__((aligned(16))) float s_scores[BS];
-  __shared__ int s_hist[PART ? 1 : kSchedKeys];
+  // WAVES wavefronts share one (sequence, head[, partition]): wavefront w
+  // takes the w-th contiguous share of its tiles; the states merge in LDS.
+  constexpr int NSTATE = NLOAD + 2;
+  __shared__ __attribute__((aligned(16))) float s_scores_all[WAVES * BS];
+  __shared__ int s_hist[PART ? 1 : WAVES * kSchedKeys];
+  __shared__ float s_state[WAVES > 1 ? (WAVES - 1) * kWave * NSTATE : 1];
 
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  float* s_scores = s_scores_all + wave * BS;
   const int H = p.num_heads;
   int h, s, part;
   if constexpr (PART) {
@@ -186,8 +195,9 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
                         : (int)blockIdx.x;
     const int rank = pos / H;
     h = pos % H;
-    s = p.order_by_length ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist, lane)
-                          : rank;
+    s = p.order_by_length
+            ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist + wave * kSchedKeys, lane)
+            : rank;
     part = 0;
   }
   const int L = p.context_lens[s];
@@ -198,7 +208,11 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   const int seq_tiles = (L + BS - 1) / BS;
   const int tile0 = PART ? part * tiles_per_part : 0;
   if (PART && L > 0 && tile0 >= seq_tiles) return;
-  const int ntiles = PART ? min(seq_tiles - tile0, tiles_per_part) : seq_tiles;
+  const int ntiles_all = PART ? min(seq_tiles - tile0, tiles_per_part) : seq_tiles;
+  const int share = (ntiles_all + WAVES - 1) / WAVES;
+  const int my_first = tile0 + wave * share;          // first tile of this wavefront
+  const int ntiles = max(0, min(share, ntiles_all - wave * share));
+  const int last_tile = tile0 + ntiles_all - 1;       // the only tile that can be partial
   const bool bad_len = (L < 0) || (L > MB * BS);
 
   // output row addressing
@@ -219,7 +233,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   };
 
   if (bad_len || (PART && L <= 0 && !bad_len)) {
-    if (bad_len) {
+    if (bad_len && wave == 0) {
       float nanv[NLOAD];
 #pragma unroll
       for (int i = 0; i < NLOAD; ++i) nanv[i] = __builtin_nanf("");
@@ -243,7 +257,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE_BYTES;
   const int64_t block_stride = (int64_t)p.num_kv_heads * TILE_BYTES;
   TableWindow tw;
-  tw.init(p.block_table + (int64_t)s * MB + tile0, ntiles, p.num_blocks, lane);
+  tw.init(p.block_table + (int64_t)s * MB + my_first, ntiles, p.num_blocks, lane);
 
   u32x4_t kb[NBUF][NLOAD];
   u32x4_t vb[NBUF][NLOAD];
@@ -274,7 +288,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   const int c_k = lane % LPT;          // K: chunk of the token's dims
   const int tok_k = lane / LPT;        // K: token within an instruction
   const int tok_v = (lane % LPR) * VEC;  // V: first token of this lane's columns
-  const int last_len = L - (tile0 + ntiles - 1) * BS;   // valid tokens in the last tile
+  const int last_len = L - last_tile * BS;   // valid tokens in the last tile
 
   auto process = [&](const u32x4_t (&kd)[NLOAD], const u32x4_t (&vd)[NLOAD], bool masked) {
     // scores of tokens i*TPI + tok_k
@@ -364,7 +378,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
       const int n = n0 + u;
       issue(kb[(u + NBUF - 1) % NBUF], vb[(u + NBUF - 1) % NBUF], n + NBUF - 1);
       if (n < ntiles) {
-        const bool masked = (n == ntiles - 1) && (last_len < BS);
+        const bool masked = (my_first + n == last_tile) && (last_len < BS);
         process(kb[u], vb[u], masked);
       }
     }
@@ -397,11 +411,42 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
     }
   }
 
+  bool bad = tw.bad;
+  if constexpr (WAVES > 1) {
+    // merge the wavefronts' states (lane i holds the same rows in every one)
+    if (wave > 0) {
+      float* st = s_state + ((wave - 1) * kWave + lane) * NSTATE;
+#pragma unroll
+      for (int i = 0; i < NLOAD; ++i) st[i] = acc[i];
+      st[NLOAD] = m;
+      st[NLOAD + 1] = bad ? -l - 1.0f : l;   // sign marks a bad table entry
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+      const float* st = s_state + ((w - 1) * kWave + lane) * NSTATE;
+      const float mo = st[NLOAD];
+      float lo = st[NLOAD + 1];
+      if (lo < 0.0f) {
+        bad = true;
+        lo = -lo - 1.0f;
+      }
+      const float mn = fmaxf(m, mo);
+      const float fa = (m == mn) ? 1.0f : exp2_hw(m - mn);
+      const float fb = (mo == mn) ? 1.0f : exp2_hw(mo - mn);
+      l = l * fa + lo * fb;
+#pragma unroll
+      for (int i = 0; i < NLOAD; ++i) acc[i] = acc[i] * fa + st[i] * fb;
+      m = mn;
+    }
+  }
+
   float res[NLOAD];
-  if (tw.bad) {
+  if (bad) {
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) res[i] = __builtin_nanf("");
-  } else if (ntiles <= 0) {
+  } else if (ntiles_all <= 0) {
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) res[i] = 0.0f;
   } else {
@@ -412,23 +457,25 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeParams p) {
   if constexpr (PART) {
     if (lane == 0) {
       const int64_t idx = (int64_t)row * p.num_partitions + part;
-      p.max_logits[idx] = tw.bad ? __builtin_nanf("") : m * kLn2;
-      p.exp_sums[idx] = tw.bad ? __builtin_nanf("") : l;
+      p.max_logits[idx] = bad ? __builtin_nanf("") : m * kLn2;
+      p.exp_sums[idx] = bad ? __builtin_nanf("") : l;
     }
   }
 }
 
-template <typename QT, typename CT, int D, int BS, bool PART>
+template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid = PART ? dim3(p.num_heads, p.num_seqs, p.num_partitions)
                         : dim3(p.num_heads * p.num_seqs, 1, 1);
-  hipLaunchKernelGGL((decode_valu_kernel<QT, CT, D, BS, PART>), grid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((decode_valu_kernel<QT, CT, D, BS, PART, WAVES>), grid, dim3(64 * WAVES), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 template <typename QT, typename CT, int D, int BS>
 hipError_t pick_part(const DecodeParams& p, bool part, hipStream_t st) {
-  return part ? launch_one<QT, CT, D, BS, true>(p, st) : launch_one<QT, CT, D, BS, false>(p, st);
+  return part ? launch_one<QT, CT, D, BS, true, 1>(p, st)
+              : launch_one<QT, CT, D, BS, false, PA_VALU_WAVES>(p, st);
 }
 
 template <typename QT, typename CT, int D>
