@@ -37,5 +37,6 @@ from .paged_attention import (  # noqa: F401
     partition_partials,
     softmax_stats,
     token_slots,
+    v_tiles_to_rows,
     validate,
 )

@@ -9,9 +9,11 @@ What is computed, and where the pages define it:
   j*BS .. j*BS+BS-1) to a physical block of the pool; -1 marks an unallocated
   entry.  ("How does paged attention work (in detail)", section 2 and 4.1;
   "Paged attention" wiki, decode-path example; vLLM paper summary, section 2.)
-* Cache layouts (this library's): k_cache [NB, KVH, BS, D] and
-  v_cache [NB, KVH, D, BS]; the V tile is the value-cache layout of the vLLM
-  "Paged Attention" design page (section "Input parameters").
+* Cache layouts (this library's; the pages do not fix one):
+  k_cache [NB, KVH, BS, D]: a tile is token-major;
+  v_cache [NB, KVH, BS/4, D, 4]: a tile holds, for each group of 4
+  consecutive tokens, the D head dims, each with those 4 tokens' values
+  (token t, dim d at [t // 4, d, t % 4]).
 * Scores: x_t = scale * <q, k_t> over the whole head ("Paged Attention" design
   page, section "QK").
 * Softmax: m = max_t x_t, f_t = exp(x_t - m), l = sum_t f_t, p = f / l
@@ -96,6 +98,12 @@ def next_slot(block_table_row: np.ndarray, context_len: int, block_size: int) ->
 # ----------------------------------------------------------------------------
 # gather + attention
 
+def v_tiles_to_rows(vt: np.ndarray) -> np.ndarray:
+    """V tiles [n, BS/4, D, 4] -> rows [n * BS, D] in token order."""
+    n, q4, D, four = vt.shape
+    return np.transpose(vt, (0, 1, 3, 2)).reshape(n * q4 * four, D)
+
+
 def gather_kv(k_cache: np.ndarray, v_cache: np.ndarray, block_table_row: np.ndarray,
               context_len: int, block_size: int, kv_head: int):
     """Contiguous fp64 K, V [L, D] of one sequence and kv head, read through
@@ -104,10 +112,10 @@ def gather_kv(k_cache: np.ndarray, v_cache: np.ndarray, block_table_row: np.ndar
     nblk = num_logical_blocks(L, block_size)
     ids = np.asarray(block_table_row[:nblk], dtype=np.int64)
     K = k_cache[ids, kv_head]                      # [nblk, BS, D]
-    V = v_cache[ids, kv_head]                      # [nblk, D, BS]
+    V = v_cache[ids, kv_head]                      # [nblk, BS/4, D, 4]
     D = K.shape[-1]
     K = K.reshape(nblk * block_size, D)[:L]
-    V = np.transpose(V, (0, 2, 1)).reshape(nblk * block_size, D)[:L]
+    V = v_tiles_to_rows(V)[:L]
     return K, V
 
 
@@ -154,9 +162,9 @@ def decode_sequence(q_s: np.ndarray, k_cache, v_cache, table_row, context_len: i
         kvh = h // G
         if kvh not in cached:
             Kt = _chunk_cache(k_cache, cache_fmt, k_scale, ids, kvh)      # [nblk, BS, D]
-            Vt = _chunk_cache(v_cache, cache_fmt, v_scale, ids, kvh)      # [nblk, D, BS]
+            Vt = _chunk_cache(v_cache, cache_fmt, v_scale, ids, kvh)      # [nblk, BS/4, D, 4]
             K = Kt.reshape(nblk * block_size, D)[:L]
-            V = np.transpose(Vt, (0, 2, 1)).reshape(nblk * block_size, D)[:L]
+            V = v_tiles_to_rows(Vt)[:L]
             cached = {kvh: (K, V)}
         K, V = cached[kvh]
         x = np.float64(np.float32(scale)) * (K @ q_s[h])
@@ -241,7 +249,7 @@ def paged_decode_partitioned(q, k_cache, v_cache, block_table, context_lens, sca
             Kt = _chunk_cache(k_cache, cache_fmt, k_scale, ids, kvh)
             Vt = _chunk_cache(v_cache, cache_fmt, v_scale, ids, kvh)
             K = Kt.reshape(nblk * block_size, D)[:L]
-            V = np.transpose(Vt, (0, 2, 1)).reshape(nblk * block_size, D)[:L]
+            V = v_tiles_to_rows(Vt)[:L]
             pp = partition_partials(q_s[h], K, V, scale, partition_size)
             parts[(s, h)] = pp
             merged = merge_partials(pp)
@@ -283,7 +291,7 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, cache_fmt
         else:
             kk, vv = k[i], v[i]
         kc[b, :, o, :] = kk
-        vc[b, :, :, o] = vv
+        vc[b, :, o // 4, :, o % 4] = vv
     return kc, vc
 
 

@@ -95,7 +95,7 @@ def _i32(*ts):
 def cache_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                 slot_mapping: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0,
                 stream=None) -> None:
-    """k, v [T, KVH, D] (f16/bf16); caches [NB, KVH, BS, D] / [NB, KVH, D, BS]."""
+    """k, v [T, KVH, D] (f16/bf16); caches [NB, KVH, BS, D] / [NB, KVH, BS/4, D, 4]."""
     _dev(k, v, k_cache, v_cache, slot_mapping)
     _contig(k_cache, v_cache, slot_mapping)
     _i32(slot_mapping)
@@ -116,8 +116,8 @@ def _decode_args(q, k_cache, v_cache, block_table, context_lens):
     if q.stride(2) != 1 or q.stride(1) != D:
         raise PagedAttentionError("q rows must be [H, D] contiguous")
     NB, KVH, BS, D2 = k_cache.shape
-    if D2 != D or tuple(v_cache.shape) != (NB, KVH, D, BS):
-        raise PagedAttentionError("cache shapes must be [NB, KVH, BS, D] and [NB, KVH, D, BS]")
+    if D2 != D or tuple(v_cache.shape) != (NB, KVH, BS // 4, D, 4):
+        raise PagedAttentionError("cache shapes must be [NB, KVH, BS, D] and [NB, KVH, BS/4, D, 4]")
     return S, H, D, NB, KVH, BS
 
 

@@ -4,8 +4,8 @@
 // manager maps the token's logical block (position // block_size) to a
 // physical block and the token goes to its position inside it ("How does
 // paged attention work (in detail)", section 4.1; vLLM paper summary,
-// section 3 "Decoding").  K rows are contiguous in a K tile ([BS][D]); a V
-// row is a column of the V tile ([D][BS]).
+// section 3 "Decoding").  K rows are contiguous in a K tile ([BS][D]); in a
+// V tile ([BS/4][D][4]) token t's dim d sits at (t/4*D + d)*4 + t%4.
 //
 // One thread per (token, kv head, 8 consecutive head dims): a 16-byte load
 // of k and of v, one 16-byte (8-byte for fp8) K store and 8 V element stores.
@@ -70,11 +70,12 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams
   if constexpr (CT::kBytes == 2) {
     uint16_t* kc = reinterpret_cast<uint16_t*>(p.k_cache) + tile + (int64_t)off * D + c * 8;
     *reinterpret_cast<u32x4_t*>(kc) = kw;
-    uint16_t* vc = reinterpret_cast<uint16_t*>(p.v_cache) + tile + (int64_t)(c * 8) * BS + off;
+    uint16_t* vc = reinterpret_cast<uint16_t*>(p.v_cache) + tile +
+                   ((int64_t)(off >> 2) * D + c * 8) * 4 + (off & 3);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t w = vw[j >> 1];
-      vc[(int64_t)j * BS] = (uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+      vc[(int64_t)j * 4] = (uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFFu));
     }
   } else {
     uint32_t kq[2] = {0u, 0u};
@@ -85,10 +86,11 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteParams
     }
     uint8_t* kc = reinterpret_cast<uint8_t*>(p.k_cache) + tile + (int64_t)off * D + c * 8;
     *reinterpret_cast<u32x2_t*>(kc) = u32x2_t{kq[0], kq[1]};
-    uint8_t* vc = reinterpret_cast<uint8_t*>(p.v_cache) + tile + (int64_t)(c * 8) * BS + off;
+    uint8_t* vc = reinterpret_cast<uint8_t*>(p.v_cache) + tile +
+                  ((int64_t)(off >> 2) * D + c * 8) * 4 + (off & 3);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      vc[(int64_t)j * BS] = (uint8_t)e4m3fn_encode(in_elem<IT>(vw, j) * p.v_inv_scale);
+      vc[(int64_t)j * 4] = (uint8_t)e4m3fn_encode(in_elem<IT>(vw, j) * p.v_inv_scale);
     }
   }
 }

@@ -120,6 +120,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
   constexpr int TILE_BYTES = BS * D * ESZ;
   constexpr int NQK = D / 32;               // QK products per sub-tile
   constexpr int NPV = D / 16;               // PV products per sub-tile
+  constexpr int E = 16 / (4 * ESZ);         // head dims per 16-byte V load (4 tokens each)
+  constexpr int NVL = NPV / E;              // 16-byte V loads per sub-tile
   constexpr int NKL = ESZ == 2 ? NQK : NQK / 2;   // 16-byte K loads per sub-tile
   constexpr int NBUF = PA_MFMA_NBUF;
   static_assert(BS % 16 == 0 && D % 64 == 0, "shape");
@@ -170,18 +172,35 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
   const int h = kvh * G + n;
   const int64_t prow = (int64_t)(s * H + h) * (PART ? p.num_partitions : 1) + part;
 
+  // Output row m of product j is head dim 16E(j/E) + E m + j%E, so lane (n, g)
+  // holds, for each i, the 4E consecutive dims starting at 16E i + 4E g:
+  // dim offset E r + e comes from product E i + e, row 4g + r.
   auto write_out = [&](const float4_t (&o)[NPV]) {
     if (!head_ok) return;
 #pragma unroll
-    for (int j = 0; j < NPV; ++j) {
-      const int d = 16 * j + 4 * g;
+    for (int i = 0; i < NVL; ++i) {
+      float run[4 * E];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) run[E * r + e] = o[E * i + e][r];
+      const int d0 = 16 * E * i + 4 * E * g;
       if constexpr (PART) {
-        *reinterpret_cast<float4_t*>(p.tmp_out + prow * D + d) = o[j];
+#pragma unroll
+        for (int c = 0; c < E; ++c)
+          *reinterpret_cast<float4_t*>(p.tmp_out + prow * D + d0 + 4 * c) =
+              float4_t{run[4 * c], run[4 * c + 1], run[4 * c + 2], run[4 * c + 3]};
       } else {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + (int64_t)(s * H + h) * D + d;
-        const uint32_t w0 = (uint32_t)to_bits16<QT>(o[j][0]) | ((uint32_t)to_bits16<QT>(o[j][1]) << 16);
-        const uint32_t w1 = (uint32_t)to_bits16<QT>(o[j][2]) | ((uint32_t)to_bits16<QT>(o[j][3]) << 16);
-        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w0, w1};
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + (int64_t)(s * H + h) * D + d0;
+#pragma unroll
+        for (int c = 0; c < E / 2; ++c) {
+          uint32_t w[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            w[k] = (uint32_t)to_bits16<QT>(run[8 * c + 2 * k]) |
+                   ((uint32_t)to_bits16<QT>(run[8 * c + 2 * k + 1]) << 16);
+          *reinterpret_cast<u32x4_t*>(dst + 8 * c) = u32x4_t{w[0], w[1], w[2], w[3]};
+        }
       }
     }
   };
@@ -227,15 +246,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
     for (int i = 0; i < NKL; ++i)
       koff[u][i] = (uint32_t)((16 * u + n) * D * ESZ +
                               (ESZ == 2 ? qk_dim<2>(i, g) * 2 : 64 * i + 16 * g));
-  auto voff = [&](int u, int j) -> uint32_t {
-    return (uint32_t)((16 * j + n) * BS * ESZ + (16 * u + 4 * g) * ESZ);
-  };
+  // V tile [BS/4][D][4]: lane (n, g) reads, for load i of sub-tile u, the 16
+  // bytes of token quad 4u + g at head dims E(16 i + n) .. E(16 i + n) + E - 1
+  uint32_t voff[SUB][NVL];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u)
+#pragma unroll
+    for (int i = 0; i < NVL; ++i)
+      voff[u][i] = (uint32_t)(((4 * u + g) * D + E * (16 * i + n)) * 4 * ESZ);
 
-  using VReg = typename std::conditional<ESZ == 2, u32x2_t, uint32_t>::type;
   u32x4_t kb[NBUF][SUB][NKL];
-  VReg vb[NBUF][SUB][NPV];
+  u32x4_t vb[NBUF][SUB][NVL];
 
-  auto issue = [&](u32x4_t (&kd)[SUB][NKL], VReg (&vd)[SUB][NPV], int t) {
+  auto issue = [&](u32x4_t (&kd)[SUB][NKL], u32x4_t (&vd)[SUB][NVL], int t) {
     int phys = 0;
     uint32_t bytes = 0;
     if (t < ntiles) {
@@ -252,10 +275,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
-      for (int j = 0; j < NPV; ++j) {
-        if constexpr (ESZ == 2) vd[u][j] = buffer_load8(rv, voff(u, j));
-        else vd[u][j] = buffer_load4(rv, voff(u, j));
-      }
+      for (int i = 0; i < NVL; ++i) vd[u][i] = buffer_load16(rv, voff[u][i]);
   };
 
   // Softmax state of head n, base 2.  m is the reference the weights are
@@ -286,16 +306,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
                      M::pack_exact(b0[0], b0[1]), M::pack_exact(b1[0], b1[1])};
     }
   };
-  auto v_operand = [&](const VReg& v) -> u32x2_t {
+  // A operand of product j = E i + e: head dim row E(16 i + n) + e, tokens
+  // 4g .. 4g+3 of the sub-tile, as four 16-bit values
+  auto v_operand = [&](const u32x4_t& w, int e) -> u32x2_t {
     if constexpr (ESZ == 2) {
-      return v;
+      return u32x2_t{w[2 * e], w[2 * e + 1]};
     } else {
+      const uint32_t v = w[e];
       const float2_t v0 = fp8x2_to_f32<false>(v), v1 = fp8x2_to_f32<true>(v);
       return u32x2_t{M::pack_exact(v0[0], v0[1]), M::pack_exact(v1[0], v1[1])};
     }
   };
 
-  auto process = [&](const u32x4_t (&kd)[SUB][NKL], const VReg (&vd)[SUB][NPV], bool masked) {
+  auto process = [&](const u32x4_t (&kd)[SUB][NKL], const u32x4_t (&vd)[SUB][NVL], bool masked) {
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       float4_t sc = {0.f, 0.f, 0.f, 0.f};
@@ -337,7 +360,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
       }
 #pragma unroll
       for (int j = 0; j < NPV; ++j) {
-        u32x2_t a = v_operand(vd[u][j]);
+        u32x2_t a = v_operand(vd[u][j / E], j % E);
         if (masked) a = u32x2_t{a[0] & keep0, a[1] & keep1};
         acc[j] = M::pv(a, pb, acc[j]);
       }

@@ -8,28 +8,31 @@
 // sum of V.  The design page's CUDA kernel is prior art only; this kernel is
 // laid out for 64-lane wavefronts:
 //
-//  * One wavefront = one workgroup = one (sequence, head[, partition]).
+//  * A workgroup of WAVES wavefronts takes one (sequence, head[, partition]);
+//    wavefront w streams the w-th contiguous share of its tiles and the
+//    states merge in LDS at the end.
 //  * A (block, kv head) tile is contiguous in HBM: K [BS][D] token-major and
-//    V [D][BS] dim-major.  Each lane issues 16-byte raw buffer loads at
-//    lane*16 + i*1024, so every load instruction moves one contiguous KiB.
+//    V [BS/4][D][4] (each group of four tokens holds the D head dims, each
+//    with the four tokens' values).  Each lane issues 16-byte raw buffer loads
+//    at lane*16 + i*1024, so every load instruction moves one contiguous KiB.
 //    The tile's descriptor base is the tile address; a zero-length descriptor
 //    turns prefetches past the end of the range into free zero fills, so the
 //    prefetch pipeline (NBUF tiles in flight) needs no branches.
 //  * QK: a lane holds VEC consecutive dims of one token; D/VEC lanes reduce
 //    the dot product with DPP row operations.
-//  * The scores go through 64-256 bytes of LDS to the lanes that hold the
-//    matching V columns: a V lane owns NLOAD rows (head dims) over VEC tokens.
-//  * Softmax is online and private to each lane (running max m, sum l and
-//    the NLOAD partial outputs, in base 2: scores are pre-multiplied by
-//    scale * log2(e) and 2^x is the hardware v_exp_f32).  The lanes that
-//    share a row merge (m, l, acc) once at the end, with DPP.
-//  * Tokens past the context (last, partial tile only) are excluded by
-//    selects, never by multiplying with zero, so stale or NaN slots have no
-//    influence.
-//  * The block-table slice is read 64 entries at a time into one VGPR and
-//    broadcast per tile with v_readlane; the next 64 are loaded a chunk ahead.
-//    Ids outside [0, num_blocks) are replaced by 0 before any address is
-//    formed and make the row NaN.
+//  * Softmax is online with one reference max per wavefront (base 2: scores
+//    are pre-multiplied by scale * log2(e) and 2^x is v_exp_f32).  The
+//    reference only moves when a logit exceeds it by more than 2^8 (a ballot
+//    decides, then one wave-wide max and a rescale), so the usual tile costs
+//    one exponential per token and no cross-lane traffic besides LDS.
+//  * The weights of a tile go through LDS to the V lanes: a V lane owns E
+//    whole head dims (E = 2 for 16-bit, 4 for fp8 caches) over its token
+//    quads, so partial outputs of lanes that share dims just add at the end.
+//  * Tokens past the context (last, partial tile only) get weight 0 and
+//    their V values are skipped by selects, never multiplied by zero, so
+//    stale or NaN slots have no influence.
+//  * The block table comes through the shared TableWindow (64 entries per
+//    VGPR, v_readlane per tile); bad entries give a NaN row, never a read.
 #include "pa_decode_common.h"
 #include "pa_kernels.h"
 
@@ -89,24 +92,16 @@ __device__ __forceinline__ QFrag<CT, D> load_q(const void* qrow, int c) {
 template <typename CT, int D>
 __device__ __forceinline__ float dot_chunk(const QFrag<CT, D>& q, u32x4_t k) {
   if constexpr (__is_same(CT, F16)) {
-    float a = __builtin_amdgcn_fdot2(as_half2(q.w[0]),
-                                     as_half2(k[0]), 0.0f, false);
-    a = __builtin_amdgcn_fdot2(as_half2(q.w[1]),
-                               as_half2(k[1]), a, false);
-    a = __builtin_amdgcn_fdot2(as_half2(q.w[2]),
-                               as_half2(k[2]), a, false);
-    a = __builtin_amdgcn_fdot2(as_half2(q.w[3]),
-                               as_half2(k[3]), a, false);
+    float a = __builtin_amdgcn_fdot2(as_half2(q.w[0]), as_half2(k[0]), 0.0f, false);
+    a = __builtin_amdgcn_fdot2(as_half2(q.w[1]), as_half2(k[1]), a, false);
+    a = __builtin_amdgcn_fdot2(as_half2(q.w[2]), as_half2(k[2]), a, false);
+    a = __builtin_amdgcn_fdot2(as_half2(q.w[3]), as_half2(k[3]), a, false);
     return a;
   } else if constexpr (__is_same(CT, BF16)) {
-    float a = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(q.w[0]),
-                                              as_bf162(k[0]), 0.0f, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(q.w[1]),
-                                        as_bf162(k[1]), a, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(q.w[2]),
-                                        as_bf162(k[2]), a, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(q.w[3]),
-                                        as_bf162(k[3]), a, false);
+    float a = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(q.w[0]), as_bf162(k[0]), 0.0f, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(q.w[1]), as_bf162(k[1]), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(q.w[2]), as_bf162(k[2]), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(q.w[3]), as_bf162(k[3]), a, false);
     return a;
   } else {
     float a = 0.0f;
@@ -123,39 +118,47 @@ __device__ __forceinline__ float dot_chunk(const QFrag<CT, D>& q, u32x4_t k) {
   }
 }
 
-// Element j of a 16-byte V chunk as fp32.
-template <typename CT>
-__device__ __forceinline__ float v_elem(const u32x4_t& v, int j) {
-  if constexpr (__is_same(CT, F16)) {
-    return (j & 1) ? f16_hi(v[j >> 1]) : f16_lo(v[j >> 1]);
-  } else if constexpr (__is_same(CT, BF16)) {
-    return (j & 1) ? bf16_hi(v[j >> 1]) : bf16_lo(v[j >> 1]);
-  } else {
-    float2_t pr = ((j >> 1) & 1) ? fp8x2_to_f32<true>(v[j >> 2]) : fp8x2_to_f32<false>(v[j >> 2]);
-    return pr[j & 1];
-  }
-}
-
-template <typename CT>
-__device__ __forceinline__ void v_decode(const u32x4_t& v, float (&out)[16 / CT::kBytes]) {
-  constexpr int VEC = 16 / CT::kBytes;
+// The E x 4 values of one 16-byte V chunk (E head dims, 4 tokens each), fp32:
+// out[e][r] = dim e of the chunk, token r of the quad.
+template <typename CT, int E>
+__device__ __forceinline__ void v_chunk(const u32x4_t& w, float (&out)[E][4]) {
   if constexpr (CT::kBytes == 1) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      float2_t lo = fp8x2_to_f32<false>(v[w]);
-      float2_t hi = fp8x2_to_f32<true>(v[w]);
-      out[4 * w + 0] = lo[0];
-      out[4 * w + 1] = lo[1];
-      out[4 * w + 2] = hi[0];
-      out[4 * w + 3] = hi[1];
+    for (int e = 0; e < E; ++e) {
+      const float2_t lo = fp8x2_to_f32<false>(w[e]);
+      const float2_t hi = fp8x2_to_f32<true>(w[e]);
+      out[e][0] = lo[0];
+      out[e][1] = lo[1];
+      out[e][2] = hi[0];
+      out[e][3] = hi[1];
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) out[j] = v_elem<CT>(v, j);
+    for (int e = 0; e < E; ++e) {
+      const uint32_t a = w[2 * e], b = w[2 * e + 1];
+      if constexpr (__is_same(CT, F16)) {
+        out[e][0] = f16_lo(a);
+        out[e][1] = f16_hi(a);
+        out[e][2] = f16_lo(b);
+        out[e][3] = f16_hi(b);
+      } else {
+        out[e][0] = bf16_lo(a);
+        out[e][1] = bf16_hi(a);
+        out[e][2] = bf16_lo(b);
+        out[e][3] = bf16_hi(b);
+      }
+    }
   }
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kSlack = 8.0f;   // weights stay <= 2^8 between reference moves
 
 template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodeParams p) {
@@ -165,22 +168,21 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   constexpr int NLOAD = TILE_BYTES / 1024;  // 16-byte loads per lane per tile
   constexpr int LPT = D / VEC;              // K: lanes per token
   constexpr int TPI = kWave / LPT;          // K: tokens per load instruction
-  constexpr int LPR = BS / VEC;             // V: lanes per head-dim row
-  constexpr int RPI = kWave / LPR;          // V: rows per load instruction
-  constexpr int NBUF = PA_VALU_NBUF;        // tiles resident: 1 in use, the rest in flight
-  static_assert(NLOAD * TPI == BS && NLOAD * RPI == D, "tile mapping");
-  static_assert(LPT >= 1 && LPT <= 16 && LPR >= 1 && LPR <= 4 && NLOAD <= LPT, "lane mapping");
+  constexpr int E = 16 / (4 * ESZ);         // V: head dims per 16-byte chunk
+  constexpr int LPQ = D / E;                // V: lanes per token quad
+  constexpr int QPI = kWave / LPQ;          // V: token quads per load instruction
+  constexpr int NBUF = PA_VALU_NBUF;
+  static_assert(NLOAD * TPI == BS && NLOAD * QPI * 4 == BS, "tile mapping");
+  static_assert(LPT >= 1 && LPT <= 16 && NLOAD <= LPT && LPQ <= kWave, "lane mapping");
 
-  // WAVES wavefronts share one (sequence, head[, partition]): wavefront w
-  // takes the w-th contiguous share of its tiles; the states merge in LDS.
-  constexpr int NSTATE = NLOAD + 2;
-  __shared__ __attribute__((aligned(16))) float s_scores_all[WAVES * BS];
+  constexpr int NSTATE = E + 2;
+  __shared__ __attribute__((aligned(16))) float s_p_all[WAVES * BS];
   __shared__ int s_hist[PART ? 1 : WAVES * kSchedKeys];
   __shared__ float s_state[WAVES > 1 ? (WAVES - 1) * kWave * NSTATE : 1];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  float* s_scores = s_scores_all + wave * BS;
+  float* s_p = s_p_all + wave * BS;
   const int H = p.num_heads;
   int h, s, part;
   if constexpr (PART) {
@@ -188,8 +190,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
     s = blockIdx.y;
     part = blockIdx.z;
   } else {
-    // one pass: workgroup b takes head b % H of the sequence at position
-    // b / H of the longest-first order (or of index order)
+    // one pass: workgroup b takes head pos % H of the sequence at position
+    // pos / H of the longest-first order (or of index order)
     const int pos = p.order_by_length
                         ? snake_position((int)blockIdx.x, (int)gridDim.x, p.num_cus)
                         : (int)blockIdx.x;
@@ -203,44 +205,47 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   const int L = p.context_lens[s];
   const int MB = p.max_blocks_per_seq;
 
-  // token range of this workgroup
+  // token range of this workgroup and of this wavefront
   const int tiles_per_part = PART ? p.partition_size / BS : 0;
   const int seq_tiles = (L + BS - 1) / BS;
   const int tile0 = PART ? part * tiles_per_part : 0;
   if (PART && L > 0 && tile0 >= seq_tiles) return;
   const int ntiles_all = PART ? min(seq_tiles - tile0, tiles_per_part) : seq_tiles;
   const int share = (ntiles_all + WAVES - 1) / WAVES;
-  const int my_first = tile0 + wave * share;          // first tile of this wavefront
+  const int my_first = tile0 + wave * share;
   const int ntiles = max(0, min(share, ntiles_all - wave * share));
   const int last_tile = tile0 + ntiles_all - 1;       // the only tile that can be partial
   const bool bad_len = (L < 0) || (L > MB * BS);
 
-  // output row addressing
   const int row = s * H + h;
-  float* part_out = PART ? p.tmp_out + ((int64_t)row * p.num_partitions + part) * D : nullptr;
+  const int64_t pidx = (int64_t)row * (PART ? p.num_partitions : 1) + part;
 
-  auto write_row = [&](const float (&vals)[NLOAD], bool valid_lane) {
-    if (!valid_lane) return;
+  // lanes l < LPQ own head dims E*l .. E*l + E - 1 of the result
+  auto write_row = [&](const float (&vals)[E]) {
+    if (lane >= LPQ) return;
+    if constexpr (PART) {
+      float* dst = p.tmp_out + pidx * D + E * lane;
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i) {
-      const int d = i * RPI + lane / LPR;
-      if constexpr (PART) {
-        part_out[d] = vals[i];
-      } else {
-        reinterpret_cast<uint16_t*>(p.out)[(int64_t)row * D + d] = to_bits16<QT>(vals[i]);
+      for (int e = 0; e < E; ++e) dst[e] = vals[e];
+    } else {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + (int64_t)row * D + E * lane;
+#pragma unroll
+      for (int e = 0; e < E; e += 2) {
+        *reinterpret_cast<uint32_t*>(dst + e) =
+            (uint32_t)to_bits16<QT>(vals[e]) | ((uint32_t)to_bits16<QT>(vals[e + 1]) << 16);
       }
     }
   };
 
-  if (bad_len || (PART && L <= 0 && !bad_len)) {
+  if (bad_len || (PART && L <= 0)) {
     if (bad_len && wave == 0) {
-      float nanv[NLOAD];
+      float nanv[E];
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) nanv[i] = __builtin_nanf("");
-      write_row(nanv, lane % LPR == 0);
+      for (int e = 0; e < E; ++e) nanv[e] = __builtin_nanf("");
+      write_row(nanv);
       if (PART && lane == 0) {
-        p.max_logits[(int64_t)row * p.num_partitions + part] = __builtin_nanf("");
-        p.exp_sums[(int64_t)row * p.num_partitions + part] = __builtin_nanf("");
+        p.max_logits[pidx] = __builtin_nanf("");
+        p.exp_sums[pidx] = __builtin_nanf("");
       }
     }
     return;   // partitioned with an empty context: nothing to write
@@ -278,94 +283,64 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
     for (int i = 0; i < NLOAD; ++i) vd[i] = buffer_load16(rv, lane * 16 + i * 1024);
   };
 
-  // per-lane online softmax state (base 2)
-  float m = kNegInf;
-  float l = 0.0f;
-  float acc[NLOAD];
+  float m = kNegInf;       // reference max of this wavefront (wave-uniform)
+  float mx = kNegInf;      // exact running max of this lane's logits
+  float l = 0.0f;          // sum of this lane's token weights (its K token row)
+  float acc[E];
 #pragma unroll
-  for (int i = 0; i < NLOAD; ++i) acc[i] = 0.0f;
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
 
-  const int c_k = lane % LPT;          // K: chunk of the token's dims
-  const int tok_k = lane / LPT;        // K: token within an instruction
-  const int tok_v = (lane % LPR) * VEC;  // V: first token of this lane's columns
-  const int last_len = L - last_tile * BS;   // valid tokens in the last tile
+  const int c_k = lane % LPT;           // K: chunk of the token's dims
+  const int tok_k = lane / LPT;         // K: token within an instruction
+  const int quad_v = lane / LPQ;        // V: token quad within an instruction
+  const int last_len = L - last_tile * BS;
 
   auto process = [&](const u32x4_t (&kd)[NLOAD], const u32x4_t (&vd)[NLOAD], bool masked) {
-    // scores of tokens i*TPI + tok_k
-    float sc[NLOAD];
+    // logits of tokens i*TPI + tok_k
+    float x[NLOAD];
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
-      sc[i] = group_sum<LPT>(dot_chunk<CT, D>(qf, kd[i])) * p.qk_scale_log2;
+      x[i] = group_sum<LPT>(dot_chunk<CT, D>(qf, kd[i])) * p.qk_scale_log2;
+      if (masked) x[i] = (i * TPI + tok_k) < last_len ? x[i] : kNegInf;
     }
-    float mine = sc[0];
+    float mt = x[0];
 #pragma unroll
-    for (int i = 1; i < NLOAD; ++i) mine = (c_k == i) ? sc[i] : mine;
-    __builtin_amdgcn_wave_barrier();
-    if (c_k < NLOAD) s_scores[c_k * TPI + tok_k] = mine;
-    __builtin_amdgcn_wave_barrier();
-    float x[VEC];
-#pragma unroll
-    for (int j = 0; j < VEC; j += 4) {
-      float4_t t4 = *reinterpret_cast<const float4_t*>(&s_scores[tok_v + j]);
-      x[j] = t4[0];
-      x[j + 1] = t4[1];
-      x[j + 2] = t4[2];
-      x[j + 3] = t4[3];
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (!masked) {
-      float mt = x[0];
-#pragma unroll
-      for (int j = 1; j < VEC; ++j) mt = fmaxf(mt, x[j]);
-      const float mn = fmaxf(m, mt);
-      const float alpha = exp2_hw(m - mn);
-      m = mn;
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < NLOAD; ++i) acc[i] *= alpha;
-      float pj[VEC];
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        pj[j] = exp2_hw(x[j] - mn);
-        l += pj[j];
-      }
-#pragma unroll
-      for (int i = 0; i < NLOAD; ++i) {
-        float vv[VEC];
-        v_decode<CT>(vd[i], vv);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) acc[i] = fmaf(pj[j], vv[j], acc[i]);
-      }
-    } else {
-      bool ok[VEC];
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        ok[j] = (tok_v + j) < last_len;
-        x[j] = ok[j] ? x[j] : kNegInf;
-      }
-      float mt = x[0];
-#pragma unroll
-      for (int j = 1; j < VEC; ++j) mt = fmaxf(mt, x[j]);
-      const float mn = fmaxf(m, mt);
+    for (int i = 1; i < NLOAD; ++i) mt = fmaxf(mt, x[i]);
+    mx = fmaxf(mx, mt);
+    if (__builtin_amdgcn_ballot_w64(mt > m + kSlack) != 0) {
+      const float mn = fmaxf(m, wave_max(mt));
       const float alpha = (m == mn) ? 1.0f : exp2_hw(m - mn);
       m = mn;
       l *= alpha;
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) acc[i] *= alpha;
-      float pj[VEC];
+      for (int e = 0; e < E; ++e) acc[e] *= alpha;
+    }
+    float pw[NLOAD];
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        pj[j] = ok[j] ? exp2_hw(x[j] - mn) : 0.0f;
-        l += pj[j];
-      }
+    for (int i = 0; i < NLOAD; ++i) {
+      pw[i] = exp2_hw(x[i] - m);        // masked: 2^-inf = 0
+      l += pw[i];
+    }
+    float mine = pw[0];
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) {
-        float vv[VEC];
-        v_decode<CT>(vd[i], vv);
+    for (int i = 1; i < NLOAD; ++i) mine = (c_k == i) ? pw[i] : mine;
+    __builtin_amdgcn_wave_barrier();
+    if (c_k < NLOAD) s_p[c_k * TPI + tok_k] = mine;
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) acc[i] = ok[j] ? fmaf(pj[j], vv[j], acc[i]) : acc[i];
+    for (int i = 0; i < NLOAD; ++i) {
+      const int q = i * QPI + quad_v;                       // token quad of chunk i
+      const float4_t w4 = *reinterpret_cast<const float4_t*>(&s_p[4 * q]);
+      float v[E][4];
+      v_chunk<CT, E>(vd[i], v);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = !masked || (4 * q + r) < last_len;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = ok ? fmaf(w4[r], v[e][r], acc[e]) : acc[e];
       }
     }
+    __builtin_amdgcn_wave_barrier();
   };
 
   // prologue: NBUF - 1 tiles in flight
@@ -384,50 +359,33 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
     }
   }
 
-  // merge the lanes that share a row (they hold different token columns)
-  if constexpr (LPR >= 2) {
+  // lanes sharing head dims add up (one reference max); the weight sum adds
+  // one lane per K token row
 #pragma unroll
-    for (int step = 1; step < LPR; step *= 2) {
-      float mo, lo;
-      float ao[NLOAD];
-      if (step == 1) {
-        mo = xor_lane<1>(m);
-        lo = xor_lane<1>(l);
+  for (int o = LPQ; o < kWave; o <<= 1) {
 #pragma unroll
-        for (int i = 0; i < NLOAD; ++i) ao[i] = xor_lane<1>(acc[i]);
-      } else {
-        mo = xor_lane<2>(m);
-        lo = xor_lane<2>(l);
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) ao[i] = xor_lane<2>(acc[i]);
-      }
-      const float mn = fmaxf(m, mo);
-      const float fa = (m == mn) ? 1.0f : exp2_hw(m - mn);
-      const float fb = (mo == mn) ? 1.0f : exp2_hw(mo - mn);
-      l = l * fa + lo * fb;
-#pragma unroll
-      for (int i = 0; i < NLOAD; ++i) acc[i] = acc[i] * fa + ao[i] * fb;
-      m = mn;
-    }
+    for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
   }
+#pragma unroll
+  for (int o = LPT; o < kWave; o <<= 1) l += __shfl_xor(l, o, kWave);
 
   bool bad = tw.bad;
   if constexpr (WAVES > 1) {
-    // merge the wavefronts' states (lane i holds the same rows in every one)
+    // merge the wavefronts' states (lane i holds the same dims in every one)
     if (wave > 0) {
       float* st = s_state + ((wave - 1) * kWave + lane) * NSTATE;
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) st[i] = acc[i];
-      st[NLOAD] = m;
-      st[NLOAD + 1] = bad ? -l - 1.0f : l;   // sign marks a bad table entry
+      for (int e = 0; e < E; ++e) st[e] = acc[e];
+      st[E] = m;
+      st[E + 1] = bad ? -l - 1.0f : l;   // sign marks a bad table entry
     }
     __syncthreads();
     if (wave > 0) return;
 #pragma unroll
     for (int w = 1; w < WAVES; ++w) {
       const float* st = s_state + ((w - 1) * kWave + lane) * NSTATE;
-      const float mo = st[NLOAD];
-      float lo = st[NLOAD + 1];
+      const float mo = st[E];
+      float lo = st[E + 1];
       if (lo < 0.0f) {
         bad = true;
         lo = -lo - 1.0f;
@@ -437,28 +395,23 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
       const float fb = (mo == mn) ? 1.0f : exp2_hw(mo - mn);
       l = l * fa + lo * fb;
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) acc[i] = acc[i] * fa + st[i] * fb;
+      for (int e = 0; e < E; ++e) acc[e] = acc[e] * fa + st[e] * fb;
       m = mn;
     }
   }
 
-  float res[NLOAD];
-  if (bad) {
+  float res[E];
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i) res[i] = __builtin_nanf("");
-  } else if (ntiles_all <= 0) {
-#pragma unroll
-    for (int i = 0; i < NLOAD; ++i) res[i] = 0.0f;
-  } else {
-#pragma unroll
-    for (int i = 0; i < NLOAD; ++i) res[i] = (acc[i] / l) * p.v_scale;
+  for (int e = 0; e < E; ++e) {
+    res[e] = bad ? __builtin_nanf("") : (ntiles_all <= 0 ? 0.0f : (acc[e] / l) * p.v_scale);
   }
-  write_row(res, lane % LPR == 0);
+  write_row(res);
   if constexpr (PART) {
+    // the partial triple reports the exact max, with the sum re-referenced
+    const float mw = wave_max(mx);
     if (lane == 0) {
-      const int64_t idx = (int64_t)row * p.num_partitions + part;
-      p.max_logits[idx] = bad ? __builtin_nanf("") : m * kLn2;
-      p.exp_sums[idx] = bad ? __builtin_nanf("") : l;
+      p.max_logits[pidx] = bad ? __builtin_nanf("") : mw * kLn2;
+      p.exp_sums[pidx] = bad ? __builtin_nanf("") : (mw == m ? l : l * exp2_hw(m - mw));
     }
   }
 }

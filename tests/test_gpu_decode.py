@@ -102,7 +102,7 @@ def test_one_token_context_returns_v0_exactly():
     vc = wl.v_cache
     for s in range(wl.num_seqs):
         b = int(wl.block_table[s, 0])
-        v0 = vc[b, :, :, 0]                                 # [KVH, D]
+        v0 = vc[b, :, 0, :, 0]                              # [KVH, D]
         assert np.array_equal(bits16(out[s]), bits16(v0)), s
 
 
@@ -129,7 +129,8 @@ def test_needle_selects_its_value_exactly():
     torch.cuda.synchronize()
     for s, t in enumerate(needles):
         b = int(wl.block_table[s, t // 16])
-        assert np.array_equal(bits16(out[s]), bits16(wl.v_cache[b, :, :, t % 16])), s
+        o = t % 16
+        assert np.array_equal(bits16(out[s]), bits16(wl.v_cache[b, :, o // 4, :, o % 4])), s
 
 
 def test_relabelled_blocks_and_repeat_runs_are_bit_identical():

@@ -47,7 +47,7 @@ def test_grouped_one_token_constant_and_needle_exact():
     torch.cuda.synchronize()
     for s in range(wl.num_seqs):
         b = int(wl.block_table[s, 0])
-        v0 = wl.v_cache[b, :, :, 0].repeat_interleave(8, dim=0)         # [H, D]
+        v0 = wl.v_cache[b, :, 0, :, 0].repeat_interleave(8, dim=0)      # [H, D]
         assert np.array_equal(bits16(out[s]), bits16(v0)), s
     # constant values
     v = torch.full_like(base.v_cache, 0.8125)
@@ -68,7 +68,8 @@ def test_grouped_one_token_constant_and_needle_exact():
     for s in range(base.num_seqs):
         t = int(L[s]) - 1
         b = int(base.block_table[s, t // 16])
-        assert np.array_equal(bits16(out[s, 3]), bits16(base.v_cache[b, 0, :, t % 16])), s
+        o = t % 16
+        assert np.array_equal(bits16(out[s, 3]), bits16(base.v_cache[b, 0, o // 4, :, o % 4])), s
 
 
 @pytest.mark.parametrize("P", [16, 128])
@@ -118,9 +119,9 @@ def test_fp8_every_code_decodes_exactly(H, KVH):
     G = H // KVH
     q = torch.randn(1, H, D).to(torch.bfloat16)
     k = torch.zeros(NB, KVH, BS, D, dtype=torch.uint8)
-    v = torch.zeros(NB, KVH, D, BS, dtype=torch.uint8)
+    v = torch.zeros(NB, KVH, BS // 4, D, 4, dtype=torch.uint8)
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(2, 128)
-    v[1, :, :, 0] = codes[torch.arange(KVH) % 2]
+    v[1, :, 0, :, 0] = codes[torch.arange(KVH) % 2]
     table = torch.tensor([[1, -1]], dtype=torch.int32)
     L = torch.tensor([1], dtype=torch.int32)
     out = pa.decode(q.to(DEV), k.view(torch.float8_e4m3fn).to(DEV),

@@ -30,7 +30,7 @@ def _scatter(Kc, Vc, block_size, rng, spare=2):
     MB = max(max(need), 1) + 1
     table = -np.ones((S, MB), dtype=np.int32)
     kc = np.full((NB, KVH, block_size, D), np.nan, dtype=np.float16)
-    vc = np.full((NB, KVH, D, block_size), np.nan, dtype=np.float16)
+    vc = np.full((NB, KVH, block_size // 4, D, 4), np.nan, dtype=np.float16)
     nxt = 0
     for s in range(S):
         for j in range(need[s]):
@@ -42,7 +42,7 @@ def _scatter(Kc, Vc, block_size, rng, spare=2):
             for h in range(KVH):
                 for d in range(D):
                     kc[b, h, o, d] = Kc[s][t, h, d]
-                    vc[b, h, d, o] = Vc[s][t, h, d]
+                    vc[b, h, o // 4, d, o % 4] = Vc[s][t, h, d]
     return kc, vc, table, np.array(lens, dtype=np.int32)
 
 
@@ -79,7 +79,8 @@ def _brute(q, kc, vc, table, lens, scale, KVH, BS):
                 acc = 0.0
                 for t in range(int(lens[s])):
                     b = int(table[s][t // BS])
-                    acc += w[t] * float(vc[b, kvh, d, t % BS])
+                    o = t % BS
+                    acc += w[t] * float(vc[b, kvh, o // 4, d, o % 4])
                 out[s, h, d] = acc / tot
     return out
 
@@ -131,7 +132,7 @@ def test_bf16_and_fp8_inputs_match_sdpa_on_dequantised_values():
     qbits = (q.view(np.uint32) >> 16).astype(np.uint16)               # truncated to bf16
     qv = oracle.bf16_to_f64(qbits)
     codes_k = rng.integers(0, 256, (8, KVH, BS, D), dtype=np.uint8)
-    codes_v = rng.integers(0, 256, (8, KVH, D, BS), dtype=np.uint8)
+    codes_v = rng.integers(0, 256, (8, KVH, BS // 4, D, 4), dtype=np.uint8)
     codes_k[(codes_k & 0x7F) == 0x7F] = 0x01                           # no NaN codes
     codes_v[(codes_v & 0x7F) == 0x7F] = 0x02
     table = np.array([[3, 1, -1], [0, 6, 2]], dtype=np.int32)
@@ -144,7 +145,7 @@ def test_bf16_and_fp8_inputs_match_sdpa_on_dequantised_values():
     for s in range(S):
         rows = [(int(table[s, t // BS]), t % BS) for t in range(lens[s])]
         K = torch.stack([tk[b, :, o, :] for b, o in rows], 1)            # [KVH, L, D]
-        V = torch.stack([tv[b, :, :, o] for b, o in rows], 1)
+        V = torch.stack([tv[b, :, o // 4, :, o % 4] for b, o in rows], 1)
         K = K.repeat_interleave(H // KVH, 0)
         V = V.repeat_interleave(H // KVH, 0)
         ref = torch.nn.functional.scaled_dot_product_attention(

@@ -32,7 +32,7 @@ def test_worked_example_is_the_pages_table():
     assert wl.context_lens.tolist() == [30, 32, 70]
     assert wl.slot_mapping.tolist() == [94, 32, 198]
     assert tuple(wl.q.shape) == (3, 4, 64) and tuple(wl.k_cache.shape) == (8, 4, 32, 64)
-    assert tuple(wl.v_cache.shape) == (8, 4, 64, 32)
+    assert tuple(wl.v_cache.shape) == (8, 4, 8, 64, 4)
     _check_tables(wl)
 
 

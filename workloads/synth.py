@@ -1,10 +1,9 @@
 """Seeded synthetic inputs for paged decode attention.
 
 Cache layouts produced here (the library's layout, both row-major):
-  k_cache [num_blocks, num_kv_heads, block_size, head_size]   token-major tile
-  v_cache [num_blocks, num_kv_heads, head_size, block_size]   dim-major tile
-The V tile layout is the one the vLLM "Paged Attention" design page gives for
-its value cache (section "Input parameters"); the K tile is plain token-major.
+  k_cache [num_blocks, num_kv_heads, block_size, head_size]        token-major tile
+  v_cache [num_blocks, num_kv_heads, block_size/4, head_size, 4]   token-quad tile
+(token t, head dim d of a V tile sits at [t // 4, d, t % 4]).
 
 Every workload follows one decode step of the vLLM block manager (vLLM paper
 summary, section 3 "Decoding"; aivaro.ru "How does paged attention work",
@@ -38,7 +37,7 @@ class Workload:
     name: str
     q: torch.Tensor              # [S, H, D]  q_dtype
     k_cache: torch.Tensor        # [NB, KVH, BS, D]  cache_dtype
-    v_cache: torch.Tensor        # [NB, KVH, D, BS]  cache_dtype
+    v_cache: torch.Tensor        # [NB, KVH, BS/4, D, 4]  cache_dtype
     block_table: torch.Tensor    # [S, MB] int32, -1 = unallocated
     context_lens: torch.Tensor   # [S] int32, tokens already in the cache
     new_k: torch.Tensor          # [S, KVH, D]  q_dtype, the step's new token
@@ -141,7 +140,7 @@ def _assemble(name, ctx, table, num_blocks, gen, device, *, H, KVH, D, BS,
     tq = TORCH_DTYPES[q_dtype]
     q = _randn((S, H, D), gen, device, tq)
     k_cache = _randn((num_blocks, KVH, BS, D), gen, device, TORCH_DTYPES[cache_dtype])
-    v_cache = _randn((num_blocks, KVH, D, BS), gen, device, TORCH_DTYPES[cache_dtype])
+    v_cache = _randn((num_blocks, KVH, BS // 4, D, 4), gen, device, TORCH_DTYPES[cache_dtype])
     new_k = _randn((S, KVH, D), gen, device, tq)
     new_v = _randn((S, KVH, D), gen, device, tq)
     ctx_t = torch.tensor(ctx, dtype=torch.int32)
@@ -256,7 +255,7 @@ def fp8_shared_prefix(seed: int = 4, device: str = "cpu", num_seqs: int = 256,
     S, H, KVH, D, BS = num_seqs, num_heads, num_kv_heads, head_size, block_size
     q = _randn((S, H, D), gen, device, torch.bfloat16)
     k32 = torch.randn((nb, KVH, BS, D), generator=gen, device=device, dtype=torch.float32)
-    v32 = torch.randn((nb, KVH, D, BS), generator=gen, device=device, dtype=torch.float32)
+    v32 = torch.randn((nb, KVH, BS // 4, D, 4), generator=gen, device=device, dtype=torch.float32)
     new_k = _randn((S, KVH, D), gen, device, torch.bfloat16)
     new_v = _randn((S, KVH, D), gen, device, torch.bfloat16)
     k_amax = max(float(k32.abs().max()), float(new_k.float().abs().max()))
@@ -311,14 +310,15 @@ def poison_unused_slots(wl: Workload, covered: Optional[Sequence[int]] = None,
     k = wl.k_cache.clone()
     v = wl.v_cache.clone()
     unused = (~used).to(dev)
+    unused_v = unused.view(wl.num_blocks, BS // 4, 1, 4)[:, None]     # [NB, 1, BS/4, 1, 4]
     if wl.cache_dtype == "e4m3fn":
         kb, vb = k.view(torch.uint8), v.view(torch.uint8)
         code = 0x7F if value != value else int(torch.tensor(value).to(torch.float8_e4m3fn).view(torch.uint8))
         kb.masked_fill_(unused[:, None, :, None], code)
-        vb.masked_fill_(unused[:, None, None, :], code)
+        vb.masked_fill_(unused_v, code)
     else:
         k.masked_fill_(unused[:, None, :, None], value)
-        v.masked_fill_(unused[:, None, None, :], value)
+        v.masked_fill_(unused_v, value)
     return replace(wl, k_cache=k, v_cache=v)
 
 
