@@ -1,0 +1,140 @@
+"""The oracle's pins catch plausible mistakes: each case plants one mistake in
+the oracle (on the CPU, through monkeypatch) and checks that at least one of
+the pin tests then fails."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.formats as fmt
+import oracle.paged_attention as pa_oracle
+import test_oracle_attention as t_att
+import test_oracle_cache_write as t_cw
+import test_oracle_fp8 as t_fp8
+import test_oracle_indexing as t_idx
+
+ATTENTION_PINS = [
+    lambda: t_att.test_brute_force_tiny(0),
+    lambda: t_att.test_sdpa_library_case(8, 2),
+    lambda: t_att.test_bf16_and_fp8_inputs_match_sdpa_on_dequantised_values(),
+    lambda: t_att.test_two_tokens_closed_form(),
+    lambda: t_att.test_partition_merge_equals_unpartitioned(16),
+    lambda: t_att.test_partition_triples_against_brute_force(),
+]
+
+
+def _fails(pins) -> bool:
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert not _fails(ATTENTION_PINS)
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    orig = pa_oracle.decode_sequence
+
+    def no_scale(q_s, k_cache, v_cache, table_row, context_len, scale, *a, **kw):
+        return orig(q_s, k_cache, v_cache, table_row, context_len, 1.0, *a, **kw)
+    monkeypatch.setattr(pa_oracle, "decode_sequence", no_scale)
+    assert _fails(ATTENTION_PINS)
+
+
+def test_wrong_kv_head_mapping_is_caught(monkeypatch):
+    def interleaved(q_s, k_cache, v_cache, table_row, context_len, scale, num_kv_heads,
+                    block_size, cache_fmt, k_scale=1.0, v_scale=1.0, heads=None,
+                    return_probs=False):
+        # query head h reads kv head h % KVH instead of h // G
+        H, D = q_s.shape
+        heads = list(range(H)) if heads is None else list(heads)
+        L = int(context_len)
+        n = oracle.num_logical_blocks(L, block_size)
+        ids = np.asarray(table_row[:n], dtype=np.int64)
+        out = np.zeros((len(heads), D))
+        for i, h in enumerate(heads):
+            if L == 0:
+                continue
+            kvh = h % num_kv_heads
+            K = oracle.to_f64(k_cache[ids, kvh], cache_fmt).reshape(n * block_size, D)[:L]
+            V = oracle.v_tiles_to_rows(oracle.to_f64(v_cache[ids, kvh], cache_fmt))[:L]
+            x = np.float64(np.float32(scale)) * (K @ q_s[h])
+            _, _, p = oracle.softmax_stats(x)
+            out[i] = p @ V
+        return out
+    monkeypatch.setattr(pa_oracle, "decode_sequence", interleaved)
+    assert _fails([lambda: t_att.test_sdpa_library_case(8, 2)])
+
+
+def test_transposed_v_quad_is_caught(monkeypatch):
+    def bad_rows(vt):
+        n, q4, D, four = vt.shape
+        return vt.reshape(n * q4 * four, D)          # forgets the [quad, dim, token] order
+    monkeypatch.setattr(pa_oracle, "v_tiles_to_rows", bad_rows)
+    assert _fails(ATTENTION_PINS)
+
+
+def test_off_by_one_slot_is_caught(monkeypatch):
+    def bad_slots(row, L, bs):
+        return [(int(row[(t + 1) // bs]), (t + 1) % bs) for t in range(int(L))]
+    monkeypatch.setattr(pa_oracle, "token_slots", bad_slots)
+    monkeypatch.setattr(oracle, "token_slots", bad_slots)
+    assert _fails([t_idx.test_block_table_example_blocks_read, t_idx.test_decode_walkthrough_example])
+
+
+def test_merge_without_rescale_is_caught(monkeypatch):
+    def bad_merge(partials):
+        if not partials:
+            return None
+        w = [l for _, l, _ in partials]              # drops e^(m_p - M)
+        return sum((wi / sum(w)) * o for wi, (_, _, o) in zip(w, partials))
+    monkeypatch.setattr(pa_oracle, "merge_partials", bad_merge)
+    assert _fails([lambda: t_att.test_partition_merge_equals_unpartitioned(16)])
+
+
+def test_wrong_fp8_bias_is_caught(monkeypatch):
+    def bad_decode(codes):
+        c = codes.astype(np.int64)
+        sign = np.where(c & 0x80, -1.0, 1.0)
+        e = (c >> 3) & 0xF
+        m = (c & 0x7).astype(np.float64)
+        mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+        return sign * mag
+    monkeypatch.setattr(fmt, "e4m3fn_to_f64", bad_decode)
+    monkeypatch.setattr(oracle, "e4m3fn_to_f64", bad_decode)
+    assert _fails([t_fp8.test_decode_spot_values_from_the_definition,
+                   t_fp8.test_decode_matches_torch_on_every_code])
+
+
+def test_fp8_round_half_up_is_caught(monkeypatch):
+    import math
+
+    def bad_round(y):
+        if y != y:
+            return y
+        y = max(-448.0, min(448.0, y))
+        a = abs(y)
+        e = max(math.floor(math.log2(a)), -6) if a > 0 else -6
+        q = 2.0 ** (e - 3)
+        return math.copysign(math.floor(a / q + 0.5) * q, y)   # ties away from zero
+    monkeypatch.setattr(fmt, "e4m3fn_round", bad_round)
+    assert _fails([t_fp8.test_encode_all_fp16_inputs_brute_force_nearest])
+
+
+def test_cache_write_wrong_v_position_is_caught(monkeypatch):
+    def bad_write(k, v, k_cache, v_cache, slot_mapping, block_size, cache_fmt, k_scale=1.0,
+                  v_scale=1.0):
+        kc, vc = k_cache.copy(), v_cache.copy()
+        for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
+            if slot < 0:
+                continue
+            b, o = divmod(int(slot), block_size)
+            kc[b, :, o, :] = k[i]
+            vc[b, :, o % 4, :, o // 4 % 4] = v[i]   # quad and lane swapped
+        return kc, vc
+    monkeypatch.setattr(pa_oracle, "cache_write", bad_write)
+    monkeypatch.setattr(oracle, "cache_write", bad_write)
+    assert _fails([t_cw.test_write_then_decode_attends_the_new_token])
