@@ -27,6 +27,7 @@ from .formats import (  # noqa: F401
 )
 from .paged_attention import (  # noqa: F401
     cache_write,
+    decode_append,
     decode_sequence,
     gather_kv,
     merge_partials,
@@ -36,6 +37,7 @@ from .paged_attention import (  # noqa: F401
     paged_decode_partitioned,
     partition_partials,
     softmax_stats,
+    stored_rows,
     token_slots,
     v_tiles_to_rows,
     validate,

@@ -295,6 +295,56 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, cache_fmt
     return kc, vc
 
 
+# ----------------------------------------------------------------------------
+# one decode step: cache write and attention in one call
+
+def stored_rows(x, cache_fmt: str, scale: float = 1.0) -> np.ndarray:
+    """fp64 values a cache of cache_fmt holds for new rows x (f16 or bf16
+    bits), dequantised: 16-bit caches keep the input; e4m3fn caches hold
+    e4m3fn_encode(x, 1/scale), read back times scale."""
+    xf = to_f64(x, _fmt_of(x))
+    if cache_fmt != "e4m3fn":
+        return xf
+    codes = e4m3fn_encode(xf.astype(np.float32), inv_scale_f32(scale))
+    return _dequant(codes, cache_fmt, scale)
+
+
+def decode_append(q, k, v, k_cache, v_cache, slot_mapping, block_table, context_lens,
+                  scale: float, num_kv_heads: int, block_size: int, q_fmt: str, cache_fmt: str,
+                  k_scale: float = 1.0, v_scale: float = 1.0, seqs=None):
+    """One decode step ("How does paged attention work (in detail)", section
+    4.1: the new token's K/V is stored in its slot and the query attends over
+    the context including it; vLLM paper summary, section 3 "Decoding").
+
+    Sequence s attends over its cached positions 0 .. L-1 (through the block
+    table) followed by its new token k[s], v[s] ([KVH, D]) with the values
+    the cache stores for them.  Returns (out [S', H, D] fp64, new k_cache,
+    new v_cache), the caches as cache_write leaves them."""
+    S, H, D = q.shape
+    seqs = list(range(S)) if seqs is None else list(seqs)
+    validate(block_table[seqs], context_lens[seqs], block_size, k_cache.shape[0], H, num_kv_heads)
+    G = H // num_kv_heads
+    kc, vc = cache_write(k, v, k_cache, v_cache, slot_mapping, block_size, cache_fmt,
+                         k_scale, v_scale)
+    out = np.zeros((len(seqs), H, D), dtype=np.float64)
+    for i, s in enumerate(seqs):
+        L = int(context_lens[s])
+        q_s = to_f64(q[s], q_fmt)
+        ids = np.asarray(block_table[s, :num_logical_blocks(L, block_size)], dtype=np.int64)
+        k_new = stored_rows(k[s], cache_fmt, k_scale)            # [KVH, D]
+        v_new = stored_rows(v[s], cache_fmt, v_scale)
+        for h in range(H):
+            kvh = h // G
+            Kt = _chunk_cache(k_cache, cache_fmt, k_scale, ids, kvh)
+            Vt = _chunk_cache(v_cache, cache_fmt, v_scale, ids, kvh)
+            K = np.concatenate([Kt.reshape(-1, D)[:L], k_new[kvh][None]])
+            V = np.concatenate([v_tiles_to_rows(Vt)[:L], v_new[kvh][None]])
+            x = np.float64(np.float32(scale)) * (K @ q_s[h])
+            _, _, p = softmax_stats(x)
+            out[i, h] = p @ V
+    return out, kc, vc
+
+
 def _fmt_of(a: np.ndarray) -> str:
     if a.dtype == np.float16:
         return "f16"

@@ -138,3 +138,23 @@ def test_cache_write_wrong_v_position_is_caught(monkeypatch):
     monkeypatch.setattr(pa_oracle, "cache_write", bad_write)
     monkeypatch.setattr(oracle, "cache_write", bad_write)
     assert _fails([t_cw.test_write_then_decode_attends_the_new_token])
+
+
+def test_append_without_quantising_the_new_token_is_caught(monkeypatch):
+    import test_oracle_decode_append as t_app
+
+    def raw_rows(x, cache_fmt, scale=1.0):
+        return oracle.to_f64(x, pa_oracle._fmt_of(x))      # skips the fp8 round trip
+    monkeypatch.setattr(pa_oracle, "stored_rows", raw_rows)
+    assert _fails([lambda: t_app.test_equals_write_then_decode_one_longer("e4m3fn"),
+                   t_app.test_empty_context_gives_the_new_value])
+
+
+def test_append_that_drops_the_new_token_is_caught(monkeypatch):
+    import test_oracle_decode_append as t_app
+    orig = pa_oracle.stored_rows
+
+    def tiny_rows(x, cache_fmt, scale=1.0):
+        return orig(x, cache_fmt, scale) * 0.0               # new token contributes a zero row
+    monkeypatch.setattr(pa_oracle, "stored_rows", tiny_rows)
+    assert _fails([t_app.test_worked_example_by_hand])
