@@ -1,14 +1,16 @@
 """Benchmark of one decode step of paged attention on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1] [--unfused]
 
 A step is one pass of the hot path over one synthetic batch that is already
-resident in HBM: pa_cache_write of every sequence's new token, then decode
-attention over context_len + 1 tokens (pa_decode, or pa_decode_partitioned +
-pa_reduce for the long-context workload).  Prints one JSON line.
+resident in HBM: every sequence's new token is stored in its cache slot and
+decode attention runs over context_len + 1 tokens.  One-pass workloads do
+both in one launch (pa_decode_append; --unfused: pa_cache_write, then
+pa_decode); the long-context workload runs pa_cache_write, then
+pa_decode_partitioned + pa_reduce.  Prints one JSON line.
 
 value = KV tokens attended per second over the K timed steps (whole job).
-roofline = the decode kernel's algorithmic HBM bytes per launch / its mean
+roofline = the attention kernel's algorithmic HBM bytes per launch / its mean
 launch time (HIP events on the launch stream), against 8 TB/s.
 cpu_baseline = the CPU oracle (test infrastructure, fp64 numpy) on a bounded
 sample of the same workload, timed on this host.
@@ -40,13 +42,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, lens) -> int:
-    """K+V of every attended token, q in, out, block-table ids, context_lens."""
+def algorithmic_bytes(wl, cached_lens, append: bool) -> int:
+    """Bytes one launch of the attention kernel must move: K+V of every
+    cached token it reads, q in, out, block-table ids and context_lens; the
+    fused step adds the new tokens' K/V (read from the inputs, written to the
+    cache) and slot_mapping."""
     S, H, D, KVH, BS = wl.num_seqs, wl.num_heads, wl.head_size, wl.num_kv_heads, wl.block_size
     e_kv, e_q = ELEM_BYTES[wl.cache_dtype], ELEM_BYTES[wl.q_dtype]
-    tok = sum(lens)
-    ids = sum(-(-L // BS) for L in lens)
-    return tok * KVH * D * 2 * e_kv + 2 * S * H * D * e_q + 4 * ids + 4 * S
+    tok = sum(cached_lens)
+    ids = sum(-(-L // BS) for L in cached_lens)
+    b = tok * KVH * D * 2 * e_kv + 2 * S * H * D * e_q + 4 * ids + 4 * S
+    if append:
+        b += S * KVH * D * 2 * (e_q + e_kv) + 4 * S
+    return b
 
 
 def recorded_traffic(kernel: str, workload: str, src_hash: str):
@@ -125,6 +133,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama7b_mha",
                     choices=["worked_example", "llama7b_mha", "gqa", "long_context",
                              "fp8_shared_prefix"])
+    ap.add_argument("--unfused", action="store_true",
+                    help="one-pass workloads: pa_cache_write then pa_decode instead of the "
+                         "single pa_decode_append launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -147,6 +158,7 @@ def main(argv=None):
     lens_step = (wl.context_lens + 1).contiguous()       # the step attends the new token too
     lens_host = lens_step.cpu().tolist()
     partitioned = wl.partition_size > 0
+    fused = not partitioned and not args.unfused
     P = wl.partition_size
     max_len = max(lens_host)
     out = torch.empty_like(wl.q)
@@ -156,8 +168,9 @@ def main(argv=None):
     ev = []
 
     def step(record: bool):
-        pa.cache_write(wl.new_k, wl.new_v, wl.k_cache, wl.v_cache, wl.slot_mapping,
-                       k_scale=wl.k_scale, v_scale=wl.v_scale)
+        if not fused:
+            pa.cache_write(wl.new_k, wl.new_v, wl.k_cache, wl.v_cache, wl.slot_mapping,
+                           k_scale=wl.k_scale, v_scale=wl.v_scale)
         if record:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -165,6 +178,10 @@ def main(argv=None):
         if partitioned:
             pa.decode_partitioned_only(wl.q, wl.k_cache, wl.v_cache, wl.block_table, lens_step,
                                        wl.scale, P, max_len, ws, wl.k_scale, wl.v_scale)
+        elif fused:
+            pa.decode_append(wl.q, wl.new_k, wl.new_v, wl.k_cache, wl.v_cache, wl.slot_mapping,
+                             wl.block_table, wl.context_lens, wl.scale, k_scale=wl.k_scale,
+                             v_scale=wl.v_scale, out=out)
         else:
             pa.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, lens_step, wl.scale,
                       k_scale=wl.k_scale, v_scale=wl.v_scale, out=out)
@@ -193,9 +210,13 @@ def main(argv=None):
     tokens = sum(lens_host)
     value = tokens / (ms_per_step * 1e-3)
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-    alg = algorithmic_bytes(wl, lens_host)
+    if fused:
+        alg = algorithmic_bytes(wl, wl.context_lens.cpu().tolist(), True)
+    else:
+        alg = algorithmic_bytes(wl, lens_host, False)
     achieved = alg / (kern_ms * 1e-3) / 1e9
-    kernel = "pa_decode_partitioned" if partitioned else "pa_decode"
+    kernel = ("pa_decode_partitioned" if partitioned
+              else ("pa_decode_append" if fused else "pa_decode"))
     src_hash = kernel_source_hash()
     traffic = recorded_traffic(kernel, args.workload, src_hash)
 
@@ -224,8 +245,9 @@ def main(argv=None):
             "block_size": wl.block_size, "kv_dtype": kv_dt,
             "context_tokens_per_step": tokens,
             "partition_size": P if partitioned else None,
-            "step": "pa_cache_write + " + ("pa_decode_partitioned + pa_reduce" if partitioned
-                                           else "pa_decode"),
+            "step": ("pa_decode_append" if fused else
+                     "pa_cache_write + " + ("pa_decode_partitioned + pa_reduce" if partitioned
+                                            else "pa_decode")),
         },
         "roofline": {
             "bound": "hbm",

@@ -23,21 +23,30 @@
  *
  * Layouts (row-major, element type `cache_dtype`):
  *   k_cache [num_blocks, num_kv_heads, block_size, head_size]   token-major tile
- *   v_cache [num_blocks, num_kv_heads, head_size, block_size]   dim-major tile
+ *   v_cache [num_blocks, num_kv_heads, block_size/4, head_size, 4]
+ *           quad-interleaved tile: token t of a block, head dim d, sits at
+ *           [t / 4, d, t % 4] (four consecutive tokens of one dim are
+ *           adjacent, the dims of one token quad follow each other)
  *   q       [num_seqs, num_heads, head_size] with row stride q_seq_stride
  *   out     [num_seqs, num_heads, head_size] contiguous, element type q_dtype
  *   block_table  [num_seqs, max_blocks_per_seq] int32
  *   context_lens [num_seqs] int32: tokens attended by sequence s (positions
  *                0 .. context_lens[s]-1).  A decode step writes the new token
- *                at position L with pa_cache_write, then decodes with L + 1.
+ *                at position L with pa_cache_write, then decodes with L + 1,
+ *                or does both in one launch with pa_decode_append.
  * Query head h reads kv head h / (num_heads / num_kv_heads).
  *
  * Element types: q/out f16 or bf16; caches f16, bf16 (same type as q) or
  * fp8 e4m3fn (OCP) with one fp32 scale per cache: value = code * k_scale
  * (resp. v_scale).  Scales are ignored for 16-bit caches.
  *
+ * Alignment: q, out, k, v, the caches and tmp_out start on 16-byte
+ * boundaries and q_seq_stride / kv_token_stride are multiples of 8 elements
+ * (rows move as 16-byte pieces); anything else gives PA_ERR_SHAPE.
+ *
  * Ownership and execution: every array pointer is a device pointer owned by
- * the caller; inputs are only read; only out, the caches (pa_cache_write) and
+ * the caller; inputs are only read; only out, the caches (pa_cache_write,
+ * pa_decode_append) and
  * the workspace arrays are written.  The library allocates nothing and keeps
  * no state.  All calls are asynchronous on `stream` (a hipStream_t; NULL is
  * the default stream); a PA_OK return means "launched", not "finished".
@@ -78,7 +87,7 @@ typedef enum {
 /* Static text for a status code (never NULL). */
 const char* pa_status_string(int status);
 
-/* Version of this ABI (incremented on any signature change). */
+/* Version of this ABI (incremented on any signature or layout change). */
 int pa_abi_version(void);
 
 /*
@@ -88,7 +97,8 @@ int pa_abi_version(void);
  *   slot_mapping  [num_tokens] int32: slot = physical_block * block_size +
  *                 offset; a negative slot skips the token.
  *   Writes k[i, h, :] to k_cache[slot / BS, h, slot % BS, :] and v[i, h, :]
- *   to v_cache[slot / BS, h, :, slot % BS]; nothing else is written.
+ *   to v_cache[slot / BS, h, (slot % BS) / 4, :, slot % 4]; nothing else is
+ *   written.
  *   16-bit caches: cache_dtype == in_dtype, bits copied unchanged.
  *   fp8 cache: code = e4m3fn(clamp(x * (1/scale), -448, 448)) rounded to
  *   nearest even, with 1/scale computed once in fp32 on the host and the
@@ -121,6 +131,38 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t max_blocks_per_seq, int64_t num_blocks, int64_t q_seq_stride,
               pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale, float v_scale,
               void* stream);
+
+/*
+ * pa_decode_append — one decode step in one launch: store each sequence's
+ * new token and attend over its cached context plus that token.
+ *   k, v          [num_seqs, num_kv_heads, head_size] (row stride
+ *                 kv_token_stride elements), q_dtype: the new token of each
+ *                 sequence.
+ *   slot_mapping  [num_seqs] int32: the new token's slot (as in
+ *                 pa_cache_write; negative: not stored).
+ *   Stores k[s], v[s] exactly as pa_cache_write does, and writes
+ *   out[s, h, :] = attention of q[s, h, :] over positions
+ *   0 .. context_lens[s] - 1 of the cache (read through block_table) and
+ *   the new token, whose K/V enter with the values the cache stores for
+ *   them (fp8: quantised).  When slot_mapping[s] is the slot of position
+ *   context_lens[s] this equals pa_cache_write followed by pa_decode with
+ *   context_lens[s] + 1 (the cache-write and decode steps of the decode
+ *   phase, "How does paged attention work (in detail)", section 4.1, and the
+ *   vLLM paper summary, section 3 "Decoding").
+ *   The new token is taken from k/v, never read back from the cache.  A slot
+ *   that some sequence of the same call reads inside its context is a caller
+ *   error (the read races with the store).  Bad device data as in pa_decode:
+ *   the row is NaN; the token is still stored.
+ * Same support matrix as pa_decode (one pass only).
+ */
+int pa_decode_append(void* out, const void* q, const void* k, const void* v,
+                     void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                     const int32_t* block_table, const int32_t* context_lens,
+                     float scale, int32_t num_kv_heads, int32_t block_size,
+                     int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                     int32_t max_blocks_per_seq, int64_t num_blocks, int64_t q_seq_stride,
+                     int64_t kv_token_stride, pa_dtype q_dtype, pa_dtype cache_dtype,
+                     float k_scale, float v_scale, void* stream);
 
 /*
  * Workspace of pa_decode_partitioned, in bytes, for
@@ -163,6 +205,8 @@ int pa_decode_partitioned(const void* q, const void* k_cache, const void* v_cach
  * with NP_s = ceil(context_lens[s] / partition_size); context 0 gives zeros;
  * NP_s > max_num_partitions or a NaN partial gives a NaN row.
  *   out [num_seqs, num_heads, head_size] out_dtype (f16 or bf16).
+ *   max_num_partitions <= 15360 (one fp32 weight per partition is staged in
+ *   LDS); larger gives PA_ERR_WORKSPACE.
  */
 int pa_reduce(void* out, const float* tmp_out, const float* max_logits,
               const float* exp_sums, const int32_t* context_lens, int32_t num_seqs,

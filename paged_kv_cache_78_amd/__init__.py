@@ -5,6 +5,7 @@ from .binding import (  # noqa: F401
     PagedAttentionError,
     cache_write,
     decode,
+    decode_append,
     decode_partitioned,
     decode_partitioned_only,
     lib,

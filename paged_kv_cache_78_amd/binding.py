@@ -20,7 +20,8 @@ PA_F16, PA_BF16, PA_FP8_E4M3FN = 0, 1, 2
 _DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_FP8_E4M3FN}
 
 EXPORTS = ("pa_status_string", "pa_abi_version", "pa_cache_write", "pa_decode",
-           "pa_partition_workspace_bytes", "pa_decode_partitioned", "pa_reduce")
+           "pa_decode_append", "pa_partition_workspace_bytes", "pa_decode_partitioned",
+           "pa_reduce")
 
 
 class PagedAttentionError(RuntimeError):
@@ -47,6 +48,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i64, i64,
                             ctypes.c_int, ctypes.c_int, f32, f32, vp]
+    L.pa_decode_append.restype = ctypes.c_int
+    L.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32,
+                                   i32, i64, i64, i64, ctypes.c_int, ctypes.c_int, f32, f32, vp]
     L.pa_partition_workspace_bytes.restype = ctypes.c_size_t
     L.pa_partition_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.pa_decode_partitioned.restype = ctypes.c_int
@@ -135,6 +139,36 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            _ptr(context_lens), scale, KVH, BS, S, H, D, block_table.shape[1], NB,
                            q.stride(0), _DT[q.dtype], _DT[k_cache.dtype], k_scale, v_scale,
                            _stream(stream)), "pa_decode")
+    return out
+
+
+def decode_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                  v_cache: torch.Tensor, slot_mapping: torch.Tensor, block_table: torch.Tensor,
+                  context_lens: torch.Tensor, scale: float, k_scale: float = 1.0,
+                  v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """pa_decode_append: store each sequence's new token k[s], v[s] ([S, KVH, D]) at
+    slot_mapping[s] and attend over the cached context plus that token."""
+    S, H, D, NB, KVH, BS = _decode_args(q, k_cache, v_cache, block_table, context_lens)
+    _dev(k, v, slot_mapping)
+    _contig(slot_mapping)
+    _i32(slot_mapping)
+    if (tuple(k.shape) != (S, KVH, D) or v.shape != k.shape or v.stride() != k.stride()
+            or k.stride(2) != 1 or k.stride(1) != D):
+        raise PagedAttentionError("k and v must be [S, KVH, D] with [KVH, D] rows")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise PagedAttentionError("k and v must have q's dtype")
+    if slot_mapping.numel() != S:
+        raise PagedAttentionError("slot_mapping must hold one slot per sequence")
+    if out is None:
+        out = torch.empty((S, H, D), dtype=q.dtype, device=q.device)
+    _dev(out)
+    _contig(out)
+    _check(lib().pa_decode_append(
+        _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+        _ptr(block_table), _ptr(context_lens), scale, KVH, BS, S, H, D, block_table.shape[1], NB,
+        q.stride(0), k.stride(0), _DT[q.dtype], _DT[k_cache.dtype], k_scale, v_scale,
+        _stream(stream)), "pa_decode_append")
     return out
 
 

@@ -10,35 +10,12 @@
 // One thread per (token, kv head, 8 consecutive head dims): a 16-byte load
 // of k and of v, one 16-byte (8-byte for fp8) K store and 8 V element stores.
 //
-// fp8 caches store e4m3fn(clamp(x * inv_scale, +-448)) rounded to nearest
-// even, computed here with integer operations from the format definition
-// (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals
-// m * 2^-9, S.1111.111 = NaN, largest finite 448).
+// fp8 caches store e4m3fn_encode(x * inv_scale) (pa_device.h).
 #include "pa_device.h"
 #include "pa_kernels.h"
 
 namespace pa {
 namespace {
-
-__device__ __forceinline__ uint32_t e4m3fn_encode(float y) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  if (y != y) return sign | 0x7Fu;
-  float a = __builtin_fabsf(y);
-  a = a > 448.0f ? 448.0f : a;                 // saturate (also +-inf)
-  const uint32_t ua = __builtin_bit_cast(uint32_t, a);
-  const int e = (int)(ua >> 23) - 127;
-  if (e < -6) {
-    // below the smallest normal: quantum 2^-9; rint rounds half to even
-    const uint32_t mi = (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8 (8 = 2^-6)
-    return sign | mi;
-  }
-  // keep 3 mantissa bits, round half to even (carry may bump the exponent)
-  const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
-  const uint32_t e2 = (r >> 23) - 127u + 7u;
-  const uint32_t m3 = (r >> 20) & 7u;
-  return sign | (e2 << 3) | m3;
-}
 
 template <typename IT>
 __device__ __forceinline__ float in_elem(const u32x4_t& w, int j) {

@@ -21,10 +21,12 @@
 //    output column.
 //  * A = V^T: lane l holds head dim 16j + l%16 and tokens 4(l/16)..+3, an
 //    8-byte piece of the dim-major V tile row (4 bytes for fp8).
-//  * P is rounded to the 16-bit operand type; the softmax sum adds the same
-//    rounded weights, so weights and normaliser agree.
-//  * fp8 e4m3fn K/V convert exactly to bf16/f16 before the products; the
-//    cache scales multiply the logits (k_scale) and the output (v_scale).
+//  * P goes into the product as f16 (f16 and fp8 caches; the softmax sum
+//    adds the same rounded weights) or, for bf16 caches, split into two bf16
+//    parts hi + lo with one product each (16 bits of every weight).
+//  * fp8 e4m3fn K/V convert exactly to the q type (QK) and to f16 (PV)
+//    before the products; the cache scales multiply the logits (k_scale) and
+//    the output (v_scale).
 //  * The per-head max over a sub-tile's 16 tokens needs two cross-row
 //    exchanges; everything else stays in registers.  Tokens past the context
 //    get -inf logits and zeroed V operands (a NaN in an unused slot must not
@@ -126,13 +128,21 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
   constexpr int NBUF = PA_MFMA_NBUF;
   static_assert(BS % 16 == 0 && D % 64 == 0, "shape");
   using M = Mma<QT>;
+  // PV operand type: f16 for fp8 caches (decoded e4m3fn is exact in f16,
+  // which keeps 11 bits of each weight), else the cache's own type.  With
+  // bf16 the weights are split as P = hi + lo, two bf16 values, and PV runs
+  // once per part: a single bf16 weight carries 8 bits, too few for the
+  // output tolerance on short contexts with widely spread V values.
+  using MV = std::conditional_t<ESZ == 1, Mma<F16>, Mma<QT>>;
+  constexpr bool kSplitP = ESZ == 2 && __is_same(QT, BF16);
 
   // WAVES wavefronts share one (sequence, kv head[, partition]): wavefront w
   // takes the w-th contiguous share of its tiles; the states merge in LDS.
   constexpr int NSTATE = NPV * 4 + 4;       // floats of one lane's softmax state
   __shared__ int s_hist[PART ? 1 : WAVES * kSchedKeys];
   __shared__ float s_state[WAVES > 1 ? (WAVES - 1) * kWave * NSTATE : 1];
-  const int wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) float s_new[PART ? 4 : 2 * D];   // fused append
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;          // head column / token row of the products
   const int g = lane >> 4;          // lane group: k-block / row block
@@ -205,7 +215,20 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
     }
   };
 
+  // The step's new token (fused append) goes to the last wavefront, whose
+  // share of tiles is the smallest: it stores the token in its slot (which
+  // no workgroup of this launch reads unmasked: position L of its sequence
+  // is past the context) and takes it as its first token.
+  const bool take_new = !PART && p.append != 0 && wave == WAVES - 1;
+  NewToken<D> nt;
+  int32_t slot = -1;
+  if (take_new) slot = p.slot_mapping[s];
+
   if (bad_len || (PART && L <= 0)) {
+    if (take_new) {
+      nt.load(p, s, kvh, lane);
+      nt.template store<QT, CT, BS>(p, slot, kvh, lane, s_new);
+    }
     if (bad_len && wave == 0) {
       float4_t o[NPV];
       const float nanv = __builtin_nanf("");
@@ -314,7 +337,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
     } else {
       const uint32_t v = w[e];
       const float2_t v0 = fp8x2_to_f32<false>(v), v1 = fp8x2_to_f32<true>(v);
-      return u32x2_t{M::pack_exact(v0[0], v0[1]), M::pack_exact(v1[0], v1[1])};
+      return u32x2_t{MV::pack_exact(v0[0], v0[1]), MV::pack_exact(v1[0], v1[1])};
     }
   };
 
@@ -349,9 +372,18 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
       float pr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) pr[r] = ok[r] ? exp2_hw(x[r] - m) : 0.0f;
-      const uint32_t p01 = M::pack(pr[0], pr[1]);
-      const uint32_t p23 = M::pack(pr[2], pr[3]);
-      l += (M::lo(p01) + M::hi(p01)) + (M::lo(p23) + M::hi(p23));
+      const uint32_t p01 = MV::pack(pr[0], pr[1]);
+      const uint32_t p23 = MV::pack(pr[2], pr[3]);
+      u32x2_t pl = {0u, 0u};
+      if constexpr (kSplitP) {
+        // residuals are exact in fp32; hi + lo carries 16 bits of each weight
+        pl = u32x2_t{MV::pack(pr[0] - MV::lo(p01), pr[1] - MV::hi(p01)),
+                     MV::pack(pr[2] - MV::lo(p23), pr[3] - MV::hi(p23))};
+        l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      } else {
+        // the sum adds the rounded weights the product uses
+        l += (MV::lo(p01) + MV::hi(p01)) + (MV::lo(p23) + MV::hi(p23));
+      }
       const u32x2_t pb = {p01, p23};
       uint32_t keep0 = 0xFFFFFFFFu, keep1 = 0xFFFFFFFFu;
       if (masked) {
@@ -362,13 +394,65 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
       for (int j = 0; j < NPV; ++j) {
         u32x2_t a = v_operand(vd[u][j / E], j % E);
         if (masked) a = u32x2_t{a[0] & keep0, a[1] & keep1};
-        acc[j] = M::pv(a, pb, acc[j]);
+        acc[j] = MV::pv(a, pb, acc[j]);
+      }
+      if constexpr (kSplitP) {
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+          u32x2_t a = v_operand(vd[u][j / E], j % E);
+          if (masked) a = u32x2_t{a[0] & keep0, a[1] & keep1};
+          acc[j] = MV::pv(a, pl, acc[j]);
+        }
       }
     }
   };
 
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u) issue(kb[u], vb[u], u);
+
+  if (take_new) {
+    // store the token; its cached values land in s_new.  Logit: lane group
+    // g's q dims (qb) against the same dims of the stored K row
+    nt.load(p, s, kvh, lane);
+    nt.template store<QT, CT, BS>(p, slot, kvh, lane, s_new);
+    __builtin_amdgcn_wave_barrier();
+    float xn = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NQK; ++c) {
+      const float4_t k0 = *reinterpret_cast<const float4_t*>(s_new + qk_dim<ESZ>(c, g));
+      const float4_t k1 = *reinterpret_cast<const float4_t*>(s_new + qk_dim<ESZ>(c, g) + 4);
+      const float kk[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        xn = fmaf(M::lo(qb[c][w]), kk[2 * w], xn);
+        xn = fmaf(M::hi(qb[c][w]), kk[2 * w + 1], xn);
+      }
+    }
+    xn += __shfl_xor(xn, 16, 64);
+    xn += __shfl_xor(xn, 32, 64);
+    m = xn * p.qk_scale_log2;            // reference = its logit: weight 1
+    mx = m;
+    l = (g == 0) ? 1.0f : 0.0f;          // the four lane groups' sums add up
+    // its V row starts the accumulators: element E r + e of run i is
+    // output dim 16E i + 4E g + E r + e
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      float run[4 * E];
+#pragma unroll
+      for (int c = 0; c < E; ++c) {
+        const float4_t v4 =
+            *reinterpret_cast<const float4_t*>(s_new + D + 16 * E * i + 4 * E * g + 4 * c);
+        run[4 * c] = v4[0];
+        run[4 * c + 1] = v4[1];
+        run[4 * c + 2] = v4[2];
+        run[4 * c + 3] = v4[3];
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[E * i + e][r] = run[E * r + e];
+    }
+  }
 
   for (int t0 = 0; t0 < ntiles; t0 += NBUF) {
 #pragma unroll
@@ -422,12 +506,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodePar
 
   float4_t o[NPV];
   const float nanv = __builtin_nanf("");
+  const bool empty = ntiles_all <= 0 && (PART || p.append == 0);
+  // one division per lane; empty contexts give 0, bad ones NaN
+  const float inv = bad ? nanv : (empty ? 0.0f : p.v_scale / l);
 #pragma unroll
   for (int j = 0; j < NPV; ++j) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      o[j][r] = bad ? nanv : (ntiles_all <= 0 ? 0.0f : (acc[j][r] / l) * p.v_scale);
-    }
+    for (int r = 0; r < 4; ++r) o[j][r] = acc[j][r] * inv;   // NaN when bad
   }
   write_out(o);
   if constexpr (PART) {

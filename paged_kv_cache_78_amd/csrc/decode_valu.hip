@@ -179,8 +179,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   __shared__ __attribute__((aligned(16))) float s_p_all[WAVES * BS];
   __shared__ int s_hist[PART ? 1 : WAVES * kSchedKeys];
   __shared__ float s_state[WAVES > 1 ? (WAVES - 1) * kWave * NSTATE : 1];
+  __shared__ __attribute__((aligned(16))) float s_new[PART ? 4 : 2 * D];   // fused append
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int lane = threadIdx.x & 63;
   float* s_p = s_p_all + wave * BS;
   const int H = p.num_heads;
@@ -237,7 +238,25 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
     }
   };
 
+  // query head h reads kv head h / G (contiguous groups); this kernel is the
+  // one-head-per-kv-head path, but stays correct for any G
+  const int G = H / p.num_kv_heads;
+  const int kvh = h / G;
+  // The step's new token (fused append) goes to the last wavefront, whose
+  // share of tiles is the smallest: it takes the token as its first one,
+  // and (one query head per kv head doing it) stores it in its slot, which
+  // no workgroup of this launch reads unmasked (position L of its sequence
+  // is past the context).
+  const bool take_new = !PART && p.append != 0 && wave == WAVES - 1;
+  NewToken<D> nt;
+  int32_t slot = -1;
+  if (take_new) slot = h % G == 0 ? p.slot_mapping[s] : -1;
+
   if (bad_len || (PART && L <= 0)) {
+    if (take_new) {
+      nt.load(p, s, kvh, lane);
+      nt.template store<QT, CT, BS>(p, slot, kvh, lane, s_new);
+    }
     if (bad_len && wave == 0) {
       float nanv[E];
 #pragma unroll
@@ -251,9 +270,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
     return;   // partitioned with an empty context: nothing to write
   }
 
-  // query head h reads kv head h / G (contiguous groups); this kernel is the
-  // one-head-per-kv-head path, but stays correct for any G
-  const int kvh = h / (H / p.num_kv_heads);
   const char* qrow = reinterpret_cast<const char*>(p.q) +
                      ((int64_t)s * p.q_seq_stride + (int64_t)h * D) * sizeof(uint16_t);
   const QFrag<CT, D> qf = load_q<QT, CT, D>(qrow, lane % LPT);
@@ -347,6 +363,41 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u) issue(kb[u], vb[u], u);
 
+  if (take_new) {
+    // store the token (slot -1: another head of the group stores it); its
+    // cached values land in s_new.  Logit: the lane's q chunk against the
+    // same dims of the stored K row, summed over the LPT lanes of a row
+    nt.load(p, s, kvh, lane);
+    nt.template store<QT, CT, BS>(p, slot, kvh, lane, s_new);
+    __builtin_amdgcn_wave_barrier();
+    const float* kk = s_new + (lane % LPT) * VEC;
+    float xp = 0.0f;
+    if constexpr (CT::kBytes == 2) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float2_t k2 = *reinterpret_cast<const float2_t*>(kk + 2 * w);
+        xp = fmaf(in_lo<QT>(qf.w[w]), k2[0], xp);
+        xp = fmaf(in_hi<QT>(qf.w[w]), k2[1], xp);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) {
+        const float4_t k4 = *reinterpret_cast<const float4_t*>(kk + j);
+        xp = fmaf(qf.f[j], k4[0], xp);
+        xp = fmaf(qf.f[j + 1], k4[1], xp);
+        xp = fmaf(qf.f[j + 2], k4[2], xp);
+        xp = fmaf(qf.f[j + 3], k4[3], xp);
+      }
+    }
+    m = group_sum<LPT>(xp) * p.qk_scale_log2;   // reference = its logit: weight 1
+    mx = m;
+    if (lane < LPT) l = 1.0f;            // one K token row counts it
+    if (lane < LPQ) {                    // one token quad row adds its V
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = s_new[D + E * lane + e];
+    }
+  }
+
   for (int n0 = 0; n0 < ntiles; n0 += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
@@ -401,10 +452,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   }
 
   float res[E];
+  const bool empty = ntiles_all <= 0 && (PART || p.append == 0);
+  const float inv = bad ? __builtin_nanf("") : (empty ? 0.0f : p.v_scale / l);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    res[e] = bad ? __builtin_nanf("") : (ntiles_all <= 0 ? 0.0f : (acc[e] / l) * p.v_scale);
-  }
+  for (int e = 0; e < E; ++e) res[e] = acc[e] * inv;   // NaN when bad
   write_row(res);
   if constexpr (PART) {
     // the partial triple reports the exact max, with the sum re-referenced

@@ -29,6 +29,9 @@ int compute_units() {
   return cache[dev];
 }
 
+// The kernels move rows with 16-byte loads and stores.
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
 bool head_size_ok(int d) { return d == 64 || d == 128; }
 bool block_size_ok(int b) { return b == 16 || b == 32; }
 bool is16(pa_dtype t) { return t == PA_F16 || t == PA_BF16; }
@@ -44,7 +47,7 @@ int check_cache_types(pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale, flo
   return cache_dtype == q_dtype ? PA_OK : PA_ERR_DTYPE;
 }
 
-// Shared checks of pa_decode and pa_decode_partitioned.
+// Shared checks of pa_decode, pa_decode_append and pa_decode_partitioned.
 int check_decode(const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* block_table, const int32_t* context_lens, float scale,
                  int32_t num_kv_heads, int32_t block_size, int32_t num_seqs, int32_t num_heads,
@@ -56,7 +59,8 @@ int check_decode(const void* q, const void* k_cache, const void* v_cache,
       block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
     return PA_ERR_SHAPE;
   if (num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
-  if (q_seq_stride < (int64_t)num_heads * head_size) return PA_ERR_SHAPE;
+  if (q_seq_stride < (int64_t)num_heads * head_size || q_seq_stride % 8 != 0) return PA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
   if (num_seqs > 65535) return PA_ERR_SHAPE;   // grid dimension y (partitioned)
   if ((int64_t)num_seqs * num_heads > INT32_MAX) return PA_ERR_SHAPE;
@@ -127,7 +131,7 @@ const char* pa_status_string(int status) {
   }
 }
 
-int pa_abi_version(void) { return 1; }
+int pa_abi_version(void) { return 2; }
 
 int pa_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
                    const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
@@ -139,6 +143,8 @@ int pa_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
       num_blocks <= 0)
     return PA_ERR_SHAPE;
   if (kv_token_stride < (int64_t)num_kv_heads * head_size || kv_token_stride % 8 != 0)
+    return PA_ERR_SHAPE;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_SHAPE;
   if (!head_size_ok(head_size) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
   const int ct = check_cache_types(in_dtype, cache_dtype, k_scale, v_scale);
@@ -174,11 +180,46 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                               max_blocks_per_seq, num_blocks, q_seq_stride, q_dtype, cache_dtype,
                               k_scale, v_scale);
   if (st != PA_OK) return st;
+  if (!aligned16(out)) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   pa::DecodeParams p = make_params(q, k_cache, v_cache, block_table, context_lens, scale,
                                    num_kv_heads, num_seqs, num_heads, max_blocks_per_seq,
                                    num_blocks, q_seq_stride, cache_dtype, k_scale, v_scale);
   p.out = out;
+  const hipError_t e =
+      launch_decode(p, q_dtype, cache_dtype, head_size, block_size, false, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_decode_append(void* out, const void* q, const void* k, const void* v, void* k_cache,
+                     void* v_cache, const int32_t* slot_mapping, const int32_t* block_table,
+                     const int32_t* context_lens, float scale, int32_t num_kv_heads,
+                     int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                     int32_t max_blocks_per_seq, int64_t num_blocks, int64_t q_seq_stride,
+                     int64_t kv_token_stride, pa_dtype q_dtype, pa_dtype cache_dtype,
+                     float k_scale, float v_scale, void* stream) {
+  if (!out || !k || !v || !slot_mapping) return PA_ERR_NULL;
+  const int st = check_decode(q, k_cache, v_cache, block_table, context_lens, scale,
+                              num_kv_heads, block_size, num_seqs, num_heads, head_size,
+                              max_blocks_per_seq, num_blocks, q_seq_stride, q_dtype, cache_dtype,
+                              k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (kv_token_stride < (int64_t)num_kv_heads * head_size || kv_token_stride % 8 != 0)
+    return PA_ERR_SHAPE;
+  if (!aligned16(out) || !aligned16(k) || !aligned16(v)) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  pa::DecodeParams p = make_params(q, k_cache, v_cache, block_table, context_lens, scale,
+                                   num_kv_heads, num_seqs, num_heads, max_blocks_per_seq,
+                                   num_blocks, q_seq_stride, cache_dtype, k_scale, v_scale);
+  p.out = out;
+  p.append = 1;
+  p.k_new = k;
+  p.v_new = v;
+  p.slot_mapping = slot_mapping;
+  p.kv_token_stride = kv_token_stride;
+  const bool fp8 = cache_dtype == PA_FP8_E4M3FN;
+  p.k_inv_scale = fp8 ? 1.0f / k_scale : 1.0f;
+  p.v_inv_scale = fp8 ? 1.0f / v_scale : 1.0f;
   const hipError_t e =
       launch_decode(p, q_dtype, cache_dtype, head_size, block_size, false, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -210,6 +251,7 @@ int pa_decode_partitioned(const void* q, const void* k_cache, const void* v_cach
   if (partition_size <= 0 || partition_size % block_size != 0 || max_context_len < 0)
     return PA_ERR_WORKSPACE;
   if (!tmp_out || !max_logits || !exp_sums) return PA_ERR_NULL;
+  if (!aligned16(tmp_out)) return PA_ERR_SHAPE;
   const int64_t np = ((int64_t)max_context_len + partition_size - 1) / partition_size;
   if (np > 65535) return PA_ERR_WORKSPACE;   // grid dimension z
   if (num_seqs == 0 || np == 0) return PA_OK;
@@ -234,6 +276,7 @@ int pa_reduce(void* out, const float* tmp_out, const float* max_logits, const fl
   if (max_num_partitions > 0 && (!tmp_out || !max_logits || !exp_sums)) return PA_ERR_NULL;
   if (num_seqs < 0 || num_heads <= 0 || head_size <= 0) return PA_ERR_SHAPE;
   if (num_seqs > 65535) return PA_ERR_SHAPE;
+  if (!aligned16(out) || (max_num_partitions > 0 && !aligned16(tmp_out))) return PA_ERR_SHAPE;
   if (partition_size <= 0 || max_num_partitions < 0 || max_num_partitions > kMaxPartitions)
     return PA_ERR_WORKSPACE;
   if (!head_size_ok(head_size)) return PA_ERR_UNSUPPORTED;

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "pa_device.h"
+#include "pa_kernels.h"
 
 namespace pa {
 
@@ -133,5 +134,88 @@ __device__ __forceinline__ int snake_position(int b, int total, int units) {
   const int m = min(units, total - k * units);   // size of this stratum
   return k * units + (m - 1 - i);
 }
+
+// ---------------------------------------------------------------------------
+// Fused append: the new token of a decode step.
+
+// 16-bit input element -> fp32 (exact).
+template <typename IT>
+__device__ __forceinline__ float in_value(uint16_t bits) {
+  if constexpr (__is_same(IT, F16)) return (float)__builtin_bit_cast(_Float16, bits);
+  else return __builtin_bit_cast(float, (uint32_t)bits << 16);
+}
+// Low / high 16-bit input element of a packed pair -> fp32 (exact).
+template <typename IT>
+__device__ __forceinline__ float in_lo(uint32_t w) {
+  if constexpr (__is_same(IT, F16)) return f16_lo(w);
+  else return bf16_lo(w);
+}
+template <typename IT>
+__device__ __forceinline__ float in_hi(uint32_t w) {
+  if constexpr (__is_same(IT, F16)) return f16_hi(w);
+  else return bf16_hi(w);
+}
+
+// Row of sequence s, kv head kvh, in the new tokens' K or V input.
+__device__ __forceinline__ const uint16_t* new_token_row(const DecodeParams& p, const void* base,
+                                                         int s, int kvh, int D) {
+  return reinterpret_cast<const uint16_t*>(base) + (int64_t)s * p.kv_token_stride +
+         (int64_t)kvh * D;
+}
+
+// The new token of sequence s, kv head kvh, spread over one wavefront: lane
+// l holds dims l, l + 64, ... of its K and V input rows.
+template <int D>
+struct NewToken {
+  static constexpr int N = D / kWave;
+  uint16_t k[N];
+  uint16_t v[N];
+
+  __device__ __forceinline__ void load(const DecodeParams& p, int s, int kvh, int lane) {
+    const uint16_t* kin = new_token_row(p, p.k_new, s, kvh, D);
+    const uint16_t* vin = new_token_row(p, p.v_new, s, kvh, D);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      k[i] = kin[lane + kWave * i];
+      v[i] = vin[lane + kWave * i];
+    }
+  }
+
+  // Store the token at its slot (K row of the token-major tile; V dims at
+  // (t/4*D + d)*4 + t%4 of the quad tile) exactly as the cache write does,
+  // and put the values the cache now holds (code units, fp32) into LDS:
+  // s_kv[d] for K, s_kv[D + d] for V.
+  template <typename IT, typename CT, int BS>
+  __device__ __forceinline__ void store(const DecodeParams& p, int32_t slot, int kvh, int lane,
+                                        float* s_kv) const {
+    const int64_t blk = slot / BS;
+    const int off = slot % BS;
+    const bool write = slot >= 0 && blk < p.num_blocks;
+    const int64_t tile = (blk * p.num_kv_heads + kvh) * (int64_t)(BS * D);   // elements
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int d = lane + kWave * i;
+      const int64_t ko = tile + (int64_t)off * D + d;
+      const int64_t vo = tile + ((int64_t)(off >> 2) * D + d) * 4 + (off & 3);
+      if constexpr (CT::kBytes == 2) {
+        if (write) {
+          reinterpret_cast<uint16_t*>(const_cast<void*>(p.k_cache))[ko] = k[i];
+          reinterpret_cast<uint16_t*>(const_cast<void*>(p.v_cache))[vo] = v[i];
+        }
+        s_kv[d] = in_value<IT>(k[i]);
+        s_kv[D + d] = in_value<IT>(v[i]);
+      } else {
+        const uint32_t kc = e4m3fn_encode(in_value<IT>(k[i]) * p.k_inv_scale);
+        const uint32_t vc = e4m3fn_encode(in_value<IT>(v[i]) * p.v_inv_scale);
+        if (write) {
+          reinterpret_cast<uint8_t*>(const_cast<void*>(p.k_cache))[ko] = (uint8_t)kc;
+          reinterpret_cast<uint8_t*>(const_cast<void*>(p.v_cache))[vo] = (uint8_t)vc;
+        }
+        s_kv[d] = fp8x2_to_f32<false>(kc)[0];
+        s_kv[D + d] = fp8x2_to_f32<false>(vc)[0];
+      }
+    }
+  }
+};
 
 }  // namespace pa

@@ -132,6 +132,24 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);   // v_cvt_pk_bf16_f32 on gfx950
 }
 
+// fp32 -> OCP e4m3fn code: clamp to +-448 (saturating, also +-inf), round to
+// nearest even, NaN stays NaN; integer operations from the format definition
+// (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals m * 2^-9,
+// S.1111.111 = NaN, largest finite 1.75 * 2^8).
+__device__ __forceinline__ uint32_t e4m3fn_encode(float y) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, y) >> 24) & 0x80u;
+  const float a = __builtin_fminf(__builtin_fabsf(y), 448.0f);   // saturate (also +-inf)
+  const uint32_t ua = __builtin_bit_cast(uint32_t, a);
+  // normal range: keep 3 mantissa bits, round half to even (the carry may
+  // bump the exponent); exponent field = unbiased exponent + 7
+  const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
+  const uint32_t normal = ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u)) & 0x7Fu;
+  // below 2^-6: quantum 2^-9, rint rounds half to even (8 = 2^-6)
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
+  const uint32_t code = ua < 0x3C800000u ? sub : normal;       // 0x3C800000 = 2^-6
+  return y != y ? (sign | 0x7Fu) : (sign | code);
+}
+
 template <typename T>
 __device__ __forceinline__ uint16_t to_bits16(float x);
 template <>

@@ -14,7 +14,7 @@ struct DecodeParams {
   void* out;                 // [S, H, D] q dtype           (one pass)
   const void* q;             // [S, H, D] row stride q_seq_stride
   const void* k_cache;       // [NB, KVH, BS, D]
-  const void* v_cache;       // [NB, KVH, D, BS]
+  const void* v_cache;       // [NB, KVH, BS/4, D, 4]
   const int32_t* block_table;   // [S, MB]
   const int32_t* context_lens;  // [S]
   float* tmp_out;            // [S, H, NP, D]               (partitioned)
@@ -32,6 +32,17 @@ struct DecodeParams {
   int32_t num_partitions;    // NP (partitioned), else 1
   int32_t order_by_length;   // one pass: dispatch the longest contexts first
   int32_t num_cus;           // compute units of the device (dispatch order)
+  // fused append (one pass only): sequence s's new token k_new/v_new[s]
+  // ([KVH, D] rows, token stride kv_token_stride) is stored at
+  // slot_mapping[s] (skipped if negative) and attended after the
+  // context_lens[s] cached tokens, with the value the cache stores.
+  int32_t append;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
+  int64_t kv_token_stride;
+  float k_inv_scale;         // fp32(1/k_scale), fp8 caches
+  float v_inv_scale;
 };
 
 struct ReduceParams {

@@ -1,7 +1,10 @@
 """The five workloads at full size, in the launch configuration bench.py
-times (one decode step: cache write, then decode over context_len + 1),
-checked against the oracle on sampled (sequence, head) outputs; the whole
-output is checked for finiteness."""
+times (one decode step: the new tokens stored and attention over
+context_len + 1; one launch of pa_decode_append for the one-pass workloads,
+pa_cache_write + pa_decode_partitioned + pa_reduce for the long-context one),
+checked against the oracle on sampled (sequence, head) outputs and on the
+sampled sequences' written slots; the whole output is checked for
+finiteness.  The oracle's inputs are host copies taken before the step."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +12,8 @@ import torch
 import oracle
 import paged_kv_cache_78_amd as pa
 import workloads
-from gpu_helpers import as_f64, assert_close, oracle_arrays, sample_pairs, sampled_oracle, tol_of
+from gpu_helpers import (as_f64, assert_close, capture_step_inputs, oracle_arrays, sample_pairs,
+                         step_oracle, tol_of)
 from workloads import to_numpy_bits
 
 pytestmark = pytest.mark.gpu
@@ -17,17 +21,18 @@ DEV = "cuda:0"
 
 
 def _step(wl):
-    pa.cache_write(wl.new_k, wl.new_v, wl.k_cache, wl.v_cache, wl.slot_mapping,
-                   k_scale=wl.k_scale, v_scale=wl.v_scale)
-    lens = (wl.context_lens + 1).contiguous()
     if wl.partition_size:
+        pa.cache_write(wl.new_k, wl.new_v, wl.k_cache, wl.v_cache, wl.slot_mapping,
+                       k_scale=wl.k_scale, v_scale=wl.v_scale)
+        lens = (wl.context_lens + 1).contiguous()
         out = pa.decode_partitioned(wl.q, wl.k_cache, wl.v_cache, wl.block_table, lens, wl.scale,
                                     wl.partition_size, int(lens.max()), wl.k_scale, wl.v_scale)
     else:
-        out = pa.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, lens, wl.scale,
-                        k_scale=wl.k_scale, v_scale=wl.v_scale)
+        out = pa.decode_append(wl.q, wl.new_k, wl.new_v, wl.k_cache, wl.v_cache, wl.slot_mapping,
+                               wl.block_table, wl.context_lens, wl.scale, k_scale=wl.k_scale,
+                               v_scale=wl.v_scale)
     torch.cuda.synchronize()
-    return out, lens
+    return out
 
 
 @pytest.mark.parametrize("name,count", [("worked_example", 0), ("llama7b_mha", 12),
@@ -35,26 +40,37 @@ def _step(wl):
                                         ("long_context", 6)])
 def test_full_size_step_sampled(name, count):
     print(f"[full-size] {name}", flush=True)
+    if count == 0:
+        # small enough for the whole oracle, including both caches
+        host = workloads.make(name)
+        a = oracle_arrays(host)
+        ref, kc, vc = oracle.decode_append(
+            a["q"], to_numpy_bits(host.new_k), to_numpy_bits(host.new_v), a["k"], a["v"],
+            host.slot_mapping.numpy(), a["table"], a["lens"], host.scale, host.num_kv_heads,
+            host.block_size, host.q_dtype, host.cache_dtype)
+        wl = host.to(DEV)
+        out = _step(wl)
+        atol, rtol = tol_of(host)
+        assert_close(as_f64(out), ref, atol, rtol, name)
+        assert to_numpy_bits(wl.k_cache).tobytes() == kc.tobytes()
+        assert to_numpy_bits(wl.v_cache).tobytes() == vc.tobytes()
+        return
     if name == "long_context":
         wl = workloads.long_context(device=DEV)
     else:
         wl = workloads.make(name).to(DEV)
-    out, lens = _step(wl)
-    assert torch.isfinite(out).all()
-    atol, rtol = tol_of(wl)
-    if count == 0:
-        # small enough for the whole oracle, including the written tokens
-        host = workloads.make(name)
-        a = oracle_arrays(host)
-        kc, vc = oracle.cache_write(to_numpy_bits(host.new_k), to_numpy_bits(host.new_v), a["k"],
-                                    a["v"], host.slot_mapping.numpy(), host.block_size,
-                                    host.cache_dtype)
-        ref = oracle.paged_decode(a["q"], kc, vc, a["table"], a["lens"] + 1, host.scale,
-                                  host.num_kv_heads, host.block_size, host.q_dtype,
-                                  host.cache_dtype)
-        assert_close(as_f64(out), ref, atol, rtol, name)
-        return
     pairs = sample_pairs(wl, count)
-    ref = sampled_oracle(wl, pairs, lens)
+    captured = capture_step_inputs(wl, pairs)
+    out = _step(wl)
+    assert torch.isfinite(out).all()
+    expect = step_oracle(wl, captured)
+    atol, rtol = tol_of(wl)
     got = np.stack([as_f64(out[s, h]) for s, h in pairs])
-    assert_close(got, ref, atol, rtol, f"{name} sampled {pairs}")
+    assert_close(got, np.stack([e[0] for e in expect]), atol, rtol, f"{name} sampled {pairs}")
+    BS = wl.block_size
+    for c, (_, k_slot, v_slot) in zip(captured, expect):
+        b, o = divmod(c["slot"], BS)
+        gk = to_numpy_bits(wl.k_cache[b, c["kvh"], o])
+        gv = to_numpy_bits(wl.v_cache[b, c["kvh"], o // 4, :, o % 4])
+        assert gk.tobytes() == k_slot.tobytes(), (name, c["s"])
+        assert gv.tobytes() == v_slot.tobytes(), (name, c["s"])

@@ -158,3 +158,19 @@ def test_fp8_cache_write_bit_exact():
     assert np.array_equal(gk[~nan_k], kc[~nan_k])
     assert np.all((gk[nan_k] & 0x7F) == 0x7F)
     assert gv.tobytes() == vc.tobytes()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_grouped_short_contexts_with_spread_values(dtype):
+    """Two- to five-token contexts with V values spread by 4: the output is a
+    convex combination whose error is set by how finely each weight enters
+    the matrix product, the worst case for 16-bit weights."""
+    base = workloads.gqa(seed=31, num_seqs=16, len_range=(2, 5), num_heads=16, num_kv_heads=2,
+                         dtype=dtype)
+    v = (base.v_cache.float() * 4).to(base.v_cache.dtype)
+    k = (base.k_cache.float() * 2).to(base.k_cache.dtype)
+    wl = workloads.poison_unused_slots(workloads.synth.replace(base, v_cache=v, k_cache=k))
+    out = _decode(wl.to(DEV))
+    torch.cuda.synchronize()
+    atol, rtol = tol_of(wl)
+    assert_close(as_f64(out), oracle_decode(wl), atol, rtol, f"{dtype} short spread")
