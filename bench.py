@@ -10,8 +10,9 @@ pa_decode); the long-context workload runs pa_cache_write, then
 pa_decode_partitioned + pa_reduce.  Prints one JSON line.
 
 value = KV tokens attended per second over the K timed steps (whole job).
-roofline = the attention kernel's algorithmic HBM bytes per launch / its mean
-launch time (HIP events on the launch stream), against 8 TB/s.
+roofline = the attention kernel's algorithmic HBM bytes per launch (a block
+shared by several sequences counted once) / its mean launch time (HIP events
+on the launch stream), against 8 TB/s.
 cpu_baseline = the CPU oracle (test infrastructure, fp64 numpy) on a bounded
 sample of the same workload, timed on this host.
 """
@@ -42,14 +43,27 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, cached_lens, append: bool) -> int:
+def unique_kv_tokens(wl, cached_lens) -> int:
+    """Cached tokens counted once per physical slot: a block shared by several
+    block tables (a shared prefix) is read from HBM once per launch."""
+    table = wl.block_table.cpu().tolist()
+    BS = wl.block_size
+    used = {}
+    for s, L in enumerate(cached_lens):
+        for j in range(-(-L // BS)):
+            b = table[s][j]
+            used[b] = max(used.get(b, 0), min(BS, L - j * BS))
+    return sum(used.values())
+
+
+def algorithmic_bytes(wl, cached_lens, append: bool, unique: bool = False) -> int:
     """Bytes one launch of the attention kernel must move: K+V of every
     cached token it reads, q in, out, block-table ids and context_lens; the
     fused step adds the new tokens' K/V (read from the inputs, written to the
-    cache) and slot_mapping."""
+    cache) and slot_mapping.  unique: K+V of a shared block counted once."""
     S, H, D, KVH, BS = wl.num_seqs, wl.num_heads, wl.head_size, wl.num_kv_heads, wl.block_size
     e_kv, e_q = ELEM_BYTES[wl.cache_dtype], ELEM_BYTES[wl.q_dtype]
-    tok = sum(cached_lens)
+    tok = unique_kv_tokens(wl, cached_lens) if unique else sum(cached_lens)
     ids = sum(-(-L // BS) for L in cached_lens)
     b = tok * KVH * D * 2 * e_kv + 2 * S * H * D * e_q + 4 * ids + 4 * S
     if append:
@@ -210,10 +224,11 @@ def main(argv=None):
     tokens = sum(lens_host)
     value = tokens / (ms_per_step * 1e-3)
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-    if fused:
-        alg = algorithmic_bytes(wl, wl.context_lens.cpu().tolist(), True)
-    else:
-        alg = algorithmic_bytes(wl, lens_host, False)
+    # roofline bytes count a shared block once (it is read from HBM once);
+    # the logical count reads it once per sequence
+    cached = wl.context_lens.cpu().tolist() if fused else lens_host
+    alg = algorithmic_bytes(wl, cached, fused, unique=True)
+    alg_logical = algorithmic_bytes(wl, cached, fused)
     achieved = alg / (kern_ms * 1e-3) / 1e9
     kernel = ("pa_decode_partitioned" if partitioned
               else ("pa_decode_append" if fused else "pa_decode"))
@@ -258,6 +273,7 @@ def main(argv=None):
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": alg,
+            "logical_bytes_per_launch": alg_logical,
             "kernel_ms": kern_ms,
             "kernel_sources": src_hash,
         },
