@@ -1,4 +1,5 @@
-"""CPU oracle for paged decode attention and the KV cache write.
+"""CPU oracle for paged decode attention, the KV cache write and whole-block
+copies (copy-on-write, swapping).
 
 TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
 baseline may import anything from this package.  The GPU library never calls
@@ -12,9 +13,12 @@ of itself, by tests/test_oracle_*.py: the worked block-table examples of the
 pages, brute force on tiny inputs, scaled_dot_product_attention as a library
 special case, closed forms (one token, constant V, two tokens, q = 0, a
 needle), invariances (relabelled physical blocks, another block size,
-partition count) and an exhaustive check of the e4m3fn codec.  No function
+partition count), an exhaustive check of the e4m3fn codec, and for the block
+copies a hand-checked copy plus copy-on-write and swap scenarios whose
+attention is known.  No function
 here is "parity unpinned".
 """
+from .block_ops import copy_blocks, cow_step  # noqa: F401
 from .formats import (  # noqa: F401
     E4M3_MAX,
     bf16_to_f64,

@@ -158,3 +158,31 @@ def test_append_that_drops_the_new_token_is_caught(monkeypatch):
         return orig(x, cache_fmt, scale) * 0.0               # new token contributes a zero row
     monkeypatch.setattr(pa_oracle, "stored_rows", tiny_rows)
     assert _fails([t_app.test_worked_example_by_hand])
+
+
+def test_copy_that_forgets_v_is_caught(monkeypatch):
+    import oracle.block_ops as bo
+    import test_oracle_block_ops as t_blk
+
+    def k_only(src_k, src_v, dst_k, dst_v, mapping):
+        out_k, out_v = np.array(dst_k, copy=True), np.array(dst_v, copy=True)
+        for s, d in np.asarray(mapping).reshape(-1, 2).tolist():
+            if 0 <= s < src_k.shape[0] and 0 <= d < out_k.shape[0]:
+                out_k[d] = src_k[s]
+        return out_k, out_v
+    monkeypatch.setattr(bo, "copy_blocks", k_only)
+    monkeypatch.setattr(oracle, "copy_blocks", k_only)
+    assert _fails([t_blk.test_copy_by_hand, t_blk.test_swap_out_and_back_in_restores_the_attention])
+
+
+def test_cow_without_repointing_is_caught(monkeypatch):
+    import oracle.block_ops as bo
+    import test_oracle_block_ops as t_blk
+    orig = bo.cow_step
+
+    def no_repoint(table_row, context_len, block_size, ref_counts, free_list):
+        pair, _ = orig(table_row, context_len, block_size, ref_counts, free_list)
+        return pair, list(table_row)                 # copies but keeps writing the shared block
+    monkeypatch.setattr(bo, "cow_step", no_repoint)
+    monkeypatch.setattr(oracle, "cow_step", no_repoint)
+    assert _fails([t_blk.test_cow_then_write_keeps_the_other_sequence_and_gives_the_writer_its_token])
