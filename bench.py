@@ -139,6 +139,97 @@ def cpu_baseline(wl, lens, budget_s: float = 10.0):
                       f"KV tokens) of the same workload, fp64 numpy, {t_total:.1f} s"}
 
 
+PEAK_HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def bench_block_copy(args, torch, pa, dev):
+    """Whole-block copies on a Llama-7B-shaped pool (32 kv heads, head 128,
+    block 16, f16: 128 KiB of K and 128 KiB of V per block): 2048 pairs per
+    launch, inside one 8192-block GPU pool (copy-on-write) or between it and
+    a 2048-block pool in pinned host memory (swap out / in)."""
+    import numpy as np
+    NB, KVH, BS, D, N = 8192, 32, 16, 128, 2048
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    k = torch.randn((NB, KVH, BS, D), generator=g, device=dev, dtype=torch.float32).half()
+    v = torch.randn((NB, KVH, BS // 4, D, 4), generator=g, device=dev,
+                    dtype=torch.float32).half()
+    perm = torch.randperm(NB, generator=g, device=dev).to(torch.int32)
+    if args.op == "copy_blocks":
+        m = torch.stack([perm[:N], perm[N:2 * N]], 1).contiguous()
+        src, dst = (k, v), (k, v)
+    else:
+        hk = torch.empty((N, KVH, BS, D), dtype=torch.float16).pin_memory()
+        hv = torch.empty((N, KVH, BS // 4, D, 4), dtype=torch.float16).pin_memory()
+        hid = torch.randperm(N, generator=g, device=dev).to(torch.int32)
+        if args.op == "swap_out":
+            m = torch.stack([perm[:N], hid], 1).contiguous()
+            src, dst = (k, v), (hk, hv)
+        else:
+            m = torch.stack([hid, perm[:N]], 1).contiguous()
+            src, dst = (hk, hv), (k, v)
+    payload = N * 2 * KVH * BS * D * 2               # K + V bytes moved per launch
+
+    def launch():
+        pa.copy_blocks(src[0], src[1], dst[0], dst[1], m)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        launch()
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    if args.op == "copy_blocks":
+        alg = 2 * payload                               # read + write in HBM
+        roof = {"bound": "hbm", "peak": PEAK_HBM_GBS}
+    else:
+        alg = payload                                   # one crossing of the host link
+        roof = {"bound": "host_link", "peak": PEAK_HOST_LINK_GBS}
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    roof.update({"kernel": "pa_copy_blocks", "achieved": achieved, "unit": "GB/s",
+                 "frac": achieved / roof["peak"],
+                 "traffic": recorded_traffic("pa_copy_blocks", args.op, kernel_source_hash()),
+                 "algorithmic_bytes_per_launch": alg, "kernel_ms": kern_ms,
+                 "kernel_sources": kernel_source_hash()})
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        hk_ = k[:256].cpu().numpy()
+        hv_ = v[:256].cpu().numpy()
+        mm = np.stack([np.arange(128), np.arange(128, 256)], 1).astype(np.int32)
+        c0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - c0 < args.cpu_budget and reps < 200:
+            oracle.copy_blocks(hk_, hv_, hk_, hv_, mm)
+            reps += 1
+        dt = time.perf_counter() - c0
+        cpu = {"value": reps * 128 * 2 * KVH * BS * D * 2 / dt / 1e9, "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{reps} oracle copies of 128 blocks inside a 256-block host pool, "
+                         f"{dt:.1f} s"}
+    return {
+        "metric": f"{args.op} payload GB/s (K+V of whole blocks), 1×MI355X",
+        "value": payload / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.op}: {N} blocks of a Llama-7B-shaped pool "
+                               f"(32 kv heads, head 128, block 16, f16)",
+                   "pairs": N, "block_bytes_k_plus_v": 2 * KVH * BS * D * 2},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +238,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama7b_mha",
                     choices=["worked_example", "llama7b_mha", "gqa", "long_context",
                              "fp8_shared_prefix"])
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap_out", "swap_in"],
+                    help="step: one decode step (default); copy_blocks: copy-on-write copies "
+                         "inside a pool; swap_out / swap_in: blocks to / from a pinned host pool")
     ap.add_argument("--unfused", action="store_true",
                     help="one-pass workloads: pa_cache_write then pa_decode instead of the "
                          "single pa_decode_append launch")
@@ -168,6 +262,15 @@ def main(argv=None):
         raise SystemExit("bench.py needs a GPU (ROCm) and the built libpa.so")
     pa.lib()
     dev = "cuda:0"
+    if args.copy_calibration > 0:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.op != "step":
+        print(json.dumps(bench_block_copy(args, torch, pa, dev)))
+        return 0
     wl = make_workload(args.workload, dev)
     lens_step = (wl.context_lens + 1).contiguous()       # the step attends the new token too
     lens_host = lens_step.cpu().tolist()
@@ -205,12 +308,6 @@ def main(argv=None):
         if partitioned:
             pa.reduce(out, ws, lens_step, P)
 
-    if args.copy_calibration > 0:
-        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()

@@ -44,9 +44,9 @@
  * boundaries and q_seq_stride / kv_token_stride are multiples of 8 elements
  * (rows move as 16-byte pieces); anything else gives PA_ERR_SHAPE.
  *
- * Ownership and execution: every array pointer is a device pointer owned by
- * the caller; inputs are only read; only out, the caches (pa_cache_write,
- * pa_decode_append) and
+ * Ownership and execution: every array pointer is a device pointer
+ * (pa_copy_blocks also takes pinned host memory) owned by the caller; inputs are only read; only out, the caches (pa_cache_write,
+ * pa_decode_append, pa_copy_blocks) and
  * the workspace arrays are written.  The library allocates nothing and keeps
  * no state.  All calls are asynchronous on `stream` (a hipStream_t; NULL is
  * the default stream); a PA_OK return means "launched", not "finished".
@@ -81,7 +81,8 @@ typedef enum {
   PA_ERR_UNSUPPORTED = -3, /* head size / block size / group not built      */
   PA_ERR_DTYPE = -4,       /* element type combination not supported        */
   PA_ERR_WORKSPACE = -5,   /* partition size or workspace invalid           */
-  PA_ERR_HIP = -6          /* the HIP runtime refused the launch            */
+  PA_ERR_HIP = -6,         /* the HIP runtime refused the launch            */
+  PA_ERR_MEMORY = -7       /* a pool is not device-accessible memory        */
 } pa_status;
 
 /* Static text for a status code (never NULL). */
@@ -163,6 +164,34 @@ int pa_decode_append(void* out, const void* q, const void* k, const void* v,
                      int32_t max_blocks_per_seq, int64_t num_blocks, int64_t q_seq_stride,
                      int64_t kv_token_stride, pa_dtype q_dtype, pa_dtype cache_dtype,
                      float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_copy_blocks — copy whole physical blocks (K and V, every kv head) from
+ * one pool to another, or inside one pool.
+ *   src_k/src_v   [src_num_blocks, num_kv_heads, ...] one block = one
+ *                 contiguous run of num_kv_heads * block_size * head_size
+ *                 elements of cache_dtype in each of K and V (both cache
+ *                 layouts above).
+ *   dst_k/dst_v   [dst_num_blocks, ...] likewise.
+ *   block_mapping [num_pairs, 2] int32 (src block, dst block); a pair with a
+ *                 negative or out-of-range id is skipped.
+ *   Uses: copy-on-write of a shared block before a sequence writes into it
+ *   (src pool == dst pool; "How does paged attention work (in detail)",
+ *   section 3.3), and swapping a preempted sequence's blocks out to a CPU
+ *   pool and back (same page, section 4.3; vLLM paper summary, section 5).
+ *   Pools and block_mapping may be device memory or pinned host memory
+ *   (hipHostMalloc; the kernel reads and writes it over the host link);
+ *   pageable host memory gives PA_ERR_MEMORY.  Bytes are copied unchanged.
+ *   A dst block listed twice, or a block that is both a source and a
+ *   destination of the same call, is a caller error (unspecified result).
+ *   num_pairs <= 65535.  Supported: head_size in {64, 128}, block_size in
+ *   {16, 32}.
+ */
+int pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                   const int32_t* block_mapping, int32_t num_pairs,
+                   int64_t src_num_blocks, int64_t dst_num_blocks,
+                   int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                   pa_dtype cache_dtype, void* stream);
 
 /*
  * Workspace of pa_decode_partitioned, in bytes, for

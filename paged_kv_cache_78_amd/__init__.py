@@ -4,6 +4,7 @@ from .binding import (  # noqa: F401
     EXPORTS,
     PagedAttentionError,
     cache_write,
+    copy_blocks,
     decode,
     decode_append,
     decode_partitioned,

@@ -20,8 +20,8 @@ PA_F16, PA_BF16, PA_FP8_E4M3FN = 0, 1, 2
 _DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_FP8_E4M3FN}
 
 EXPORTS = ("pa_status_string", "pa_abi_version", "pa_cache_write", "pa_decode",
-           "pa_decode_append", "pa_partition_workspace_bytes", "pa_decode_partitioned",
-           "pa_reduce")
+           "pa_decode_append", "pa_copy_blocks", "pa_partition_workspace_bytes",
+           "pa_decode_partitioned", "pa_reduce")
 
 
 class PagedAttentionError(RuntimeError):
@@ -51,6 +51,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_append.restype = ctypes.c_int
     L.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32,
                                    i32, i64, i64, i64, ctypes.c_int, ctypes.c_int, f32, f32, vp]
+    L.pa_copy_blocks.restype = ctypes.c_int
+    L.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, ctypes.c_int,
+                                 vp]
     L.pa_partition_workspace_bytes.restype = ctypes.c_size_t
     L.pa_partition_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.pa_decode_partitioned.restype = ctypes.c_int
@@ -170,6 +173,35 @@ def decode_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cache: to
         q.stride(0), k.stride(0), _DT[q.dtype], _DT[k_cache.dtype], k_scale, v_scale,
         _stream(stream)), "pa_decode_append")
     return out
+
+
+def _pool(k: torch.Tensor, v: torch.Tensor):
+    if not ((k.is_cuda and v.is_cuda) or (k.is_pinned() and v.is_pinned())):
+        raise PagedAttentionError("a block pool must be on the GPU or in pinned host memory")
+    _contig(k, v)
+    NB, KVH, BS, D = k.shape
+    if tuple(v.shape) != (NB, KVH, BS // 4, D, 4) or v.dtype != k.dtype:
+        raise PagedAttentionError("pool shapes must be [NB, KVH, BS, D] and [NB, KVH, BS/4, D, 4]")
+    return NB, KVH, BS, D
+
+
+def copy_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor,
+                dst_v: torch.Tensor, block_mapping: torch.Tensor, stream=None) -> None:
+    """pa_copy_blocks: dst block m[i, 1] <- src block m[i, 0] (K and V, all kv
+    heads).  Pools on the GPU or in pinned host memory; block_mapping [n, 2]
+    int32 on the GPU (or pinned)."""
+    snb, kvh, bs, d = _pool(src_k, src_v)
+    dnb, kvh2, bs2, d2 = _pool(dst_k, dst_v)
+    if (kvh, bs, d) != (kvh2, bs2, d2) or src_k.dtype != dst_k.dtype:
+        raise PagedAttentionError("source and destination pools differ in block shape or dtype")
+    m = block_mapping
+    if m.dtype != torch.int32 or m.dim() != 2 or m.shape[1] != 2 or not m.is_contiguous():
+        raise PagedAttentionError("block_mapping must be a contiguous int32 [n, 2] tensor")
+    if not (m.is_cuda or m.is_pinned()):
+        raise PagedAttentionError("block_mapping must be on the GPU or in pinned host memory")
+    _check(lib().pa_copy_blocks(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(m),
+                                m.shape[0], snb, dnb, kvh, d, bs, _DT[src_k.dtype],
+                                _stream(stream)), "pa_copy_blocks")
 
 
 def partition_workspace(num_seqs: int, num_heads: int, head_size: int, max_context_len: int,

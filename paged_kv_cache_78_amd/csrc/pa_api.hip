@@ -114,6 +114,29 @@ hipError_t launch_decode(const pa::DecodeParams& p, pa_dtype q_dtype, pa_dtype c
                                 partitioned, stream);
 }
 
+// Device-side address of a pool: device and managed memory as they are,
+// pinned host memory through its device mapping.  Pageable host memory (or
+// an address the runtime does not know) gives nullptr.  A failed query's
+// error is cleared so that it cannot surface at the next launch check.
+void* device_address(const void* ptr) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, ptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  switch (a.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+      return const_cast<void*>(ptr);
+    case hipMemoryTypeHost:
+      if (!a.devicePointer || !a.hostPointer) return nullptr;
+      return reinterpret_cast<char*>(a.devicePointer) +
+             (reinterpret_cast<const char*>(ptr) - reinterpret_cast<char*>(a.hostPointer));
+    default:
+      return nullptr;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,6 +150,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_DTYPE: return "element type combination or fp8 scale not supported";
     case PA_ERR_WORKSPACE: return "invalid partition size or workspace";
     case PA_ERR_HIP: return "the HIP runtime refused the launch";
+    case PA_ERR_MEMORY: return "a pointer is not device-accessible memory (device, managed or pinned host)";
     default: return "unknown status";
   }
 }
@@ -222,6 +246,37 @@ int pa_decode_append(void* out, const void* q, const void* k, const void* v, voi
   p.v_inv_scale = fp8 ? 1.0f / v_scale : 1.0f;
   const hipError_t e =
       launch_decode(p, q_dtype, cache_dtype, head_size, block_size, false, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                   const int32_t* block_mapping, int32_t num_pairs, int64_t src_num_blocks,
+                   int64_t dst_num_blocks, int32_t num_kv_heads, int32_t head_size,
+                   int32_t block_size, pa_dtype cache_dtype, void* stream) {
+  if (!src_k || !src_v || !dst_k || !dst_v || (num_pairs > 0 && !block_mapping))
+    return PA_ERR_NULL;
+  if (num_pairs < 0 || num_pairs > 65535 || src_num_blocks <= 0 || dst_num_blocks <= 0 ||
+      num_kv_heads <= 0 || head_size <= 0 || block_size <= 0)
+    return PA_ERR_SHAPE;
+  if (!head_size_ok(head_size) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (cache_dtype != PA_F16 && cache_dtype != PA_BF16 && cache_dtype != PA_FP8_E4M3FN)
+    return PA_ERR_DTYPE;
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v))
+    return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  pa::BlockCopyParams p{};
+  p.src_k = device_address(src_k);
+  p.src_v = device_address(src_v);
+  p.dst_k = device_address(dst_k);
+  p.dst_v = device_address(dst_v);
+  p.mapping = static_cast<const int32_t*>(device_address(block_mapping));
+  if (!p.src_k || !p.src_v || !p.dst_k || !p.dst_v || !p.mapping) return PA_ERR_MEMORY;
+  p.num_pairs = num_pairs;
+  p.src_num_blocks = src_num_blocks;
+  p.dst_num_blocks = dst_num_blocks;
+  p.block_bytes = (int64_t)num_kv_heads * block_size * head_size *
+                  (cache_dtype == PA_FP8_E4M3FN ? 1 : 2);
+  const hipError_t e = pa::launch_copy_blocks(p, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

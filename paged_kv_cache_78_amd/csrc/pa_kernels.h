@@ -71,6 +71,21 @@ struct CacheWriteParams {
   float v_inv_scale;
 };
 
+// Whole-block copy between two pools (one may live in pinned host memory,
+// given by its device-side address).  mapping [num_pairs, 2] = (src, dst)
+// block ids; pairs with an id out of range are skipped.
+struct BlockCopyParams {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const int32_t* mapping;
+  int32_t num_pairs;
+  int64_t src_num_blocks;
+  int64_t dst_num_blocks;
+  int64_t block_bytes;   // bytes of one block of K (= of V), a multiple of 16
+};
+
 // Each returns hipSuccess or the launch error.  Shapes are validated by the
 // caller; the launchers only pick the instantiation.
 hipError_t launch_decode_valu(const DecodeParams& p, Dt q_dt, Dt cache_dt, int head_size,
@@ -80,5 +95,6 @@ hipError_t launch_decode_mfma(const DecodeParams& p, Dt q_dt, Dt cache_dt, int h
 hipError_t launch_reduce(const ReduceParams& p, Dt out_dt, int head_size, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteParams& p, Dt in_dt, Dt cache_dt, int head_size,
                               int block_size, hipStream_t stream);
+hipError_t launch_copy_blocks(const BlockCopyParams& p, hipStream_t stream);
 
 }  // namespace pa

@@ -130,3 +130,26 @@ def test_decode_append_rejects(kw, status):
 
 def test_decode_append_with_no_sequences_launches_nothing():
     assert _append(s=0) == 0
+
+
+def _copy(**kw):
+    import paged_kv_cache_78_amd as pa
+    a = dict(sk=FAKE, sv=FAKE, dk=FAKE, dv=FAKE, m=FAKE, n=3, snb=16, dnb=16, kvh=4, d=128, bs=16,
+             ct=0)
+    a.update(kw)
+    return pa.lib().pa_copy_blocks(a["sk"], a["sv"], a["dk"], a["dv"], a["m"], a["n"], a["snb"],
+                                   a["dnb"], a["kvh"], a["d"], a["bs"], a["ct"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sk=None), -1), (dict(dv=None), -1), (dict(m=None), -1),
+    (dict(n=-1), -2), (dict(n=70000), -2), (dict(snb=0), -2), (dict(kvh=0), -2),
+    (dict(dk=ctypes.c_void_p(0x1008)), -2),
+    (dict(d=96), -3), (dict(bs=8), -3), (dict(ct=7), -4),
+])
+def test_copy_blocks_rejects(kw, status):
+    assert _copy(**kw) == status
+
+
+def test_copy_blocks_with_no_pairs_launches_nothing():
+    assert _copy(n=0, m=None) == 0
