@@ -39,7 +39,9 @@ from .paged_attention import (  # noqa: F401
     num_logical_blocks,
     paged_decode,
     paged_decode_partitioned,
+    paged_prefill,
     partition_partials,
+    request_index,
     softmax_stats,
     stored_rows,
     token_slots,

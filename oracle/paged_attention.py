@@ -345,6 +345,60 @@ def decode_append(q, k, v, k_cache, v_cache, slot_mapping, block_table, context_
     return out, kc, vc
 
 
+# ----------------------------------------------------------------------------
+# varlen / chunked prefill over the paged cache
+
+def request_index(cu_seqlens) -> list:
+    """Request that each packed token belongs to, from cumulative lengths
+    (batching wiki, Varlen path: cu_seq_lens assigns tokens to sequences)."""
+    cu = [int(x) for x in cu_seqlens]
+    if cu[0] != 0 or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cumulative lengths must start at 0 and not decrease")
+    return [r for r in range(len(cu) - 1) for _ in range(cu[r + 1] - cu[r])]
+
+
+def paged_prefill(q, k_cache, v_cache, block_table, cu_seqlens_q, context_lens, scale: float,
+                  num_kv_heads: int, block_size: int, q_fmt: str, cache_fmt: str,
+                  k_scale: float = 1.0, v_scale: float = 1.0, causal: bool = True, seqs=None):
+    """Attention of several new query tokens per sequence over its paged K/V.
+
+    q [total_q, H, D] packs the sequences' query tokens by cu_seqlens_q
+    (batching wiki, Varlen path); sequence s has n_s = cu[s+1] - cu[s] of them
+    and context_lens[s] = K_s tokens in the cache, read through its block
+    table.  The queries are the sequence's last n_s positions (a prefill chunk
+    whose K/V were written first): query i sits at position K_s - n_s + i and,
+    causal, attends keys 0 .. K_s - n_s + i; otherwise all K_s keys.  A query
+    with no key gets zeros.  Returns out [total_q, H, D] fp64 (rows of
+    sequences not listed in seqs stay zero)."""
+    T, H, D = q.shape
+    cu = [int(x) for x in cu_seqlens_q]
+    request_index(cu)
+    S = len(cu) - 1
+    if cu[-1] != T:
+        raise ValueError("cu_seqlens_q does not cover q")
+    seqs = list(range(S)) if seqs is None else list(seqs)
+    validate(block_table[seqs], context_lens[seqs], block_size, k_cache.shape[0], H, num_kv_heads)
+    G = H // num_kv_heads
+    out = np.zeros((T, H, D), dtype=np.float64)
+    for s in seqs:
+        Ks = int(context_lens[s])
+        n = cu[s + 1] - cu[s]
+        ids = np.asarray(block_table[s, :num_logical_blocks(Ks, block_size)], dtype=np.int64)
+        for kvh in range(num_kv_heads):
+            K = _chunk_cache(k_cache, cache_fmt, k_scale, ids, kvh).reshape(-1, D)[:Ks]
+            V = v_tiles_to_rows(_chunk_cache(v_cache, cache_fmt, v_scale, ids, kvh))[:Ks]
+            for i in range(n):
+                last = Ks - n + i if causal else Ks - 1        # last key attended
+                if last < 0:
+                    continue
+                for h in range(kvh * G, (kvh + 1) * G):
+                    qv = to_f64(q[cu[s] + i, h], q_fmt)
+                    x = np.float64(np.float32(scale)) * (K[:last + 1] @ qv)
+                    _, _, p = softmax_stats(x)
+                    out[cu[s] + i, h] = p @ V[:last + 1]
+    return out
+
+
 def _fmt_of(a: np.ndarray) -> str:
     if a.dtype == np.float16:
         return "f16"

@@ -186,3 +186,46 @@ def test_cow_without_repointing_is_caught(monkeypatch):
     monkeypatch.setattr(bo, "cow_step", no_repoint)
     monkeypatch.setattr(oracle, "cow_step", no_repoint)
     assert _fails([t_blk.test_cow_then_write_keeps_the_other_sequence_and_gives_the_writer_its_token])
+
+
+def _prefill_variant(last_of):
+    """paged_prefill with another rule for the last key a query attends."""
+    def run(q, k_cache, v_cache, block_table, cu_seqlens_q, context_lens, scale, num_kv_heads,
+            block_size, q_fmt, cache_fmt, k_scale=1.0, v_scale=1.0, causal=True, seqs=None):
+        T, H, D = q.shape
+        cu = [int(x) for x in cu_seqlens_q]
+        G = H // num_kv_heads
+        out = np.zeros((T, H, D))
+        for s in range(len(cu) - 1):
+            Ks, n = int(context_lens[s]), cu[s + 1] - cu[s]
+            ids = np.asarray(block_table[s, :oracle.num_logical_blocks(Ks, block_size)],
+                             dtype=np.int64)
+            for i in range(n):
+                last = last_of(Ks, n, i) if causal else Ks - 1
+                if last < 0:
+                    continue
+                for h in range(H):
+                    K = oracle.to_f64(k_cache[ids, h // G], cache_fmt).reshape(-1, D)[:last + 1]
+                    V = oracle.v_tiles_to_rows(oracle.to_f64(v_cache[ids, h // G],
+                                                             cache_fmt))[:last + 1]
+                    x = np.float64(np.float32(scale)) * (K @ oracle.to_f64(q[cu[s] + i, h], q_fmt))
+                    _, _, p = oracle.softmax_stats(x)
+                    out[cu[s] + i, h] = p @ V
+        return out
+    return run
+
+
+def test_prefill_top_left_alignment_is_caught(monkeypatch):
+    import test_oracle_prefill as t_pf
+    bad = _prefill_variant(lambda Ks, n, i: min(i, Ks - 1))
+    monkeypatch.setattr(pa_oracle, "paged_prefill", bad)
+    monkeypatch.setattr(oracle, "paged_prefill", bad)
+    assert _fails([t_pf.test_two_chunks_equal_one, t_pf.test_example_shapes_with_causal_alignment])
+
+
+def test_prefill_off_by_one_mask_is_caught(monkeypatch):
+    import test_oracle_prefill as t_pf
+    bad = _prefill_variant(lambda Ks, n, i: Ks - n + i - 1)
+    monkeypatch.setattr(pa_oracle, "paged_prefill", bad)
+    monkeypatch.setattr(oracle, "paged_prefill", bad)
+    assert _fails([t_pf.test_brute_force_tiny, lambda: t_pf.test_sdpa_with_explicit_mask(True)])
