@@ -166,6 +166,37 @@ int pa_decode_append(void* out, const void* q, const void* k, const void* v,
                      float k_scale, float v_scale, void* stream);
 
 /*
+ * pa_prefill — varlen / chunked prefill attention over the paged cache.
+ *   q             [total_q, num_heads, head_size] (row stride q_token_stride
+ *                 elements), the query tokens of all sequences packed:
+ *                 sequence s owns rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1
+ *                 ("Paged attention" wiki, Varlen path: cu_seq_lens).
+ *   cu_seqlens_q  [num_seqs + 1] int32, cu_seqlens_q[0] = 0, non-decreasing.
+ *   context_lens  [num_seqs] int32: K_s tokens of sequence s in the cache
+ *                 (read through block_table), including the chunk's own
+ *                 tokens, which the caller wrote first (pa_cache_write).
+ *   With n_s = cu_seqlens_q[s+1] - cu_seqlens_q[s], query i of sequence s is
+ *   position K_s - n_s + i (the chunk is the sequence's last n_s tokens) and
+ *   out[cu_seqlens_q[s] + i, h, :] is its attention over keys
+ *   0 .. K_s - n_s + i (causal != 0) or over all K_s keys (causal == 0); a
+ *   query with no key gives zeros.  out [total_q, num_heads, head_size],
+ *   q_dtype, contiguous.
+ *   max_seqlen_q must bound every n_s (it sizes the grid): a larger n_s, a
+ *   bad block id in the keys read or K_s outside [0, max_blocks_per_seq *
+ *   block_size] gives NaN rows; rows of a sequence whose cu_seqlens_q range
+ *   is empty, decreasing or outside [0, total_q] are not written.
+ * Same support matrix as pa_decode (G = num_heads / num_kv_heads in [1, 16]).
+ */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* cu_seqlens_q,
+               const int32_t* context_lens, float scale, int32_t num_kv_heads,
+               int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t head_size,
+               int32_t max_blocks_per_seq, int64_t num_blocks, int32_t total_q,
+               int32_t max_seqlen_q, int64_t q_token_stride, int32_t causal,
+               pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale, float v_scale,
+               void* stream);
+
+/*
  * pa_copy_blocks — copy whole physical blocks (K and V, every kv head) from
  * one pool to another, or inside one pool.
  *   src_k/src_v   [src_num_blocks, num_kv_heads, ...] one block = one

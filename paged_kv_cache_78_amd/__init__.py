@@ -11,5 +11,6 @@ from .binding import (  # noqa: F401
     decode_partitioned_only,
     lib,
     partition_workspace,
+    prefill,
     reduce,
 )

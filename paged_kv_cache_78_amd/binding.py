@@ -20,7 +20,7 @@ PA_F16, PA_BF16, PA_FP8_E4M3FN = 0, 1, 2
 _DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_FP8_E4M3FN}
 
 EXPORTS = ("pa_status_string", "pa_abi_version", "pa_cache_write", "pa_decode",
-           "pa_decode_append", "pa_copy_blocks", "pa_partition_workspace_bytes",
+           "pa_decode_append", "pa_prefill", "pa_copy_blocks", "pa_partition_workspace_bytes",
            "pa_decode_partitioned", "pa_reduce")
 
 
@@ -51,6 +51,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_append.restype = ctypes.c_int
     L.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32,
                                    i32, i64, i64, i64, ctypes.c_int, ctypes.c_int, f32, f32, vp]
+    L.pa_prefill.restype = ctypes.c_int
+    L.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i64,
+                             i32, i32, i64, i32, ctypes.c_int, ctypes.c_int, f32, f32, vp]
     L.pa_copy_blocks.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, ctypes.c_int,
                                  vp]
@@ -172,6 +175,37 @@ def decode_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cache: to
         _ptr(block_table), _ptr(context_lens), scale, KVH, BS, S, H, D, block_table.shape[1], NB,
         q.stride(0), k.stride(0), _DT[q.dtype], _DT[k_cache.dtype], k_scale, v_scale,
         _stream(stream)), "pa_decode_append")
+    return out
+
+
+def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+            block_table: torch.Tensor, cu_seqlens_q: torch.Tensor, context_lens: torch.Tensor,
+            scale: float, max_seqlen_q: int, causal: bool = True, k_scale: float = 1.0,
+            v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+            stream=None) -> torch.Tensor:
+    """pa_prefill: packed queries q [total_q, H, D] (by cu_seqlens_q) over the
+    paged cache; returns out [total_q, H, D]."""
+    T, H, D = q.shape
+    if q.stride(2) != 1 or q.stride(1) != D:
+        raise PagedAttentionError("q rows must be [H, D] contiguous")
+    _dev(q, k_cache, v_cache, block_table, cu_seqlens_q, context_lens)
+    _contig(k_cache, v_cache, block_table, cu_seqlens_q, context_lens)
+    _i32(block_table, cu_seqlens_q, context_lens)
+    NB, KVH, BS, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != (NB, KVH, BS // 4, D, 4):
+        raise PagedAttentionError("cache shapes must be [NB, KVH, BS, D] and [NB, KVH, BS/4, D, 4]")
+    S = context_lens.numel()
+    if cu_seqlens_q.numel() != S + 1 or block_table.shape[0] != S:
+        raise PagedAttentionError("cu_seqlens_q must have num_seqs + 1 entries")
+    if out is None:
+        out = torch.empty((T, H, D), dtype=q.dtype, device=q.device)
+    _dev(out)
+    _contig(out)
+    _check(lib().pa_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cu_seqlens_q),
+        _ptr(context_lens), scale, KVH, BS, S, H, D, block_table.shape[1], NB, T, int(max_seqlen_q),
+        q.stride(0), 1 if causal else 0, _DT[q.dtype], _DT[k_cache.dtype], k_scale, v_scale,
+        _stream(stream)), "pa_prefill")
     return out
 
 

@@ -280,6 +280,47 @@ int pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* cu_seqlens_q,
+               const int32_t* context_lens, float scale, int32_t num_kv_heads,
+               int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t head_size,
+               int32_t max_blocks_per_seq, int64_t num_blocks, int32_t total_q,
+               int32_t max_seqlen_q, int64_t q_token_stride, int32_t causal, pa_dtype q_dtype,
+               pa_dtype cache_dtype, float k_scale, float v_scale, void* stream) {
+  if (!out || !cu_seqlens_q) return PA_ERR_NULL;
+  const int st = check_decode(q, k_cache, v_cache, block_table, context_lens, scale,
+                              num_kv_heads, block_size, num_seqs, num_heads, head_size,
+                              max_blocks_per_seq, num_blocks, q_token_stride, q_dtype, cache_dtype,
+                              k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (total_q < 0 || max_seqlen_q < 0 || num_kv_heads > 65535) return PA_ERR_SHAPE;
+  if (!aligned16(out)) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
+  pa::PrefillParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.context_lens = context_lens;
+  const bool fp8 = cache_dtype == PA_FP8_E4M3FN;
+  p.qk_scale_log2 = scale * (fp8 ? k_scale : 1.0f) * kLog2eHost;
+  p.v_scale = fp8 ? v_scale : 1.0f;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.q_token_stride = q_token_stride;
+  p.total_q = total_q;
+  p.max_seqlen_q = max_seqlen_q;
+  p.causal = causal ? 1 : 0;
+  const hipError_t e = pa::launch_prefill(p, to_dt(q_dtype), to_dt(cache_dtype), head_size,
+                                          block_size, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 size_t pa_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size,
                                     int32_t max_context_len, int32_t partition_size) {
   if (num_seqs < 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0 ||

@@ -71,6 +71,30 @@ struct CacheWriteParams {
   float v_inv_scale;
 };
 
+// Arguments of the prefill kernel: n_s = cu_seqlens_q[s+1] - cu_seqlens_q[s]
+// query tokens of sequence s (packed rows of q and out) attend the
+// context_lens[s] cached tokens, the queries being the last n_s positions.
+struct PrefillParams {
+  void* out;                    // [total_q, H, D] q dtype, contiguous
+  const void* q;                // [total_q, H, D] row stride q_token_stride
+  const void* k_cache;          // [NB, KVH, BS, D]
+  const void* v_cache;          // [NB, KVH, BS/4, D, 4]
+  const int32_t* block_table;   // [S, MB]
+  const int32_t* cu_seqlens_q;  // [S + 1]
+  const int32_t* context_lens;  // [S]
+  float qk_scale_log2;          // scale * k_scale * log2(e)
+  float v_scale;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int64_t num_blocks;
+  int64_t q_token_stride;
+  int32_t total_q;
+  int32_t max_seqlen_q;         // bounds every n_s (grid size)
+  int32_t causal;
+};
+
 // Whole-block copy between two pools (one may live in pinned host memory,
 // given by its device-side address).  mapping [num_pairs, 2] = (src, dst)
 // block ids; pairs with an id out of range are skipped.
@@ -96,5 +120,7 @@ hipError_t launch_reduce(const ReduceParams& p, Dt out_dt, int head_size, hipStr
 hipError_t launch_cache_write(const CacheWriteParams& p, Dt in_dt, Dt cache_dt, int head_size,
                               int block_size, hipStream_t stream);
 hipError_t launch_copy_blocks(const BlockCopyParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, Dt q_dt, Dt cache_dt, int head_size,
+                          int block_size, hipStream_t stream);
 
 }  // namespace pa

@@ -153,3 +153,30 @@ def test_copy_blocks_rejects(kw, status):
 
 def test_copy_blocks_with_no_pairs_launches_nothing():
     assert _copy(n=0, m=None) == 0
+
+
+def _prefill(**kw):
+    import paged_kv_cache_78_amd as pa
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cu=FAKE, cl=FAKE, scale=0.1, kvh=4, bs=16,
+             s=2, h=4, d=128, mb=8, nb=16, tq=10, mq=8, qs=512, causal=1, qt=0, ct=0, ks=1.0,
+             vs=1.0)
+    a.update(kw)
+    return pa.lib().pa_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cu"], a["cl"],
+                               a["scale"], a["kvh"], a["bs"], a["s"], a["h"], a["d"], a["mb"],
+                               a["nb"], a["tq"], a["mq"], a["qs"], a["causal"], a["qt"], a["ct"],
+                               a["ks"], a["vs"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), -1), (dict(cu=None), -1), (dict(q=None), -1), (dict(cl=None), -1),
+    (dict(tq=-1), -2), (dict(mq=-2), -2), (dict(qs=100), -2), (dict(h=6), -2),
+    (dict(out=ctypes.c_void_p(0x1004)), -2),
+    (dict(d=96, qs=384), -3), (dict(h=64, kvh=2, qs=64 * 128), -3),
+    (dict(qt=2), -4), (dict(ct=2, ks=0.0), -4),
+])
+def test_prefill_rejects(kw, status):
+    assert _prefill(**kw) == status
+
+
+def test_prefill_with_nothing_to_do_launches_nothing():
+    assert _prefill(tq=0) == 0 and _prefill(mq=0) == 0 and _prefill(s=0) == 0
