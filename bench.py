@@ -230,6 +230,106 @@ def bench_block_copy(args, torch, pa, dev):
     }
 
 
+PEAK_MFMA_F16_TFLOPS = 2500.0
+
+
+def prefill_flops(b) -> int:
+    """QK and PV multiply-adds of every (query, key) pair a causal chunk
+    attends: 4 * D flops per pair per query head."""
+    cu = b.cu_seqlens_q.cpu().tolist()
+    K = b.context_lens.cpu().tolist()
+    pairs = 0
+    for s in range(b.num_seqs):
+        n = cu[s + 1] - cu[s]
+        # query i attends K - n + i + 1 keys
+        pairs += n * (K[s] - n + 1) + n * (n - 1) // 2
+    return 4 * b.head_size * b.num_heads * pairs
+
+
+def bench_prefill(args, torch, pa, dev):
+    """One chunked-prefill step on the Llama-7B shape: 16 sequences, a
+    512-token chunk each after U{0..1536} cached tokens; the chunk's K/V are
+    written (pa_cache_write), then the chunk attends its context (pa_prefill,
+    causal)."""
+    import workloads
+    b = workloads.llama7b_prefill_chunks(device=dev)
+    out = torch.empty_like(b.q)
+    ev = []
+
+    def step(record):
+        pa.cache_write(b.new_k, b.new_v, b.k_cache, b.v_cache, b.slot_mapping)
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        pa.prefill(b.q, b.k_cache, b.v_cache, b.block_table, b.cu_seqlens_q, b.context_lens,
+                   b.scale, b.max_seqlen_q, out=out)
+        if record:
+            e1.record()
+            ev.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    kern_ms = sum(a.elapsed_time(c) for a, c in ev) / len(ev)
+    flops = prefill_flops(b)
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    T = int(b.q.shape[0])
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        from workloads import to_numpy_bits
+        # one sequence of the same batch, two heads' worth of work: the oracle
+        # loops over heads, so the time scales with the heads it is given
+        cu = b.cu_seqlens_q.cpu().tolist()
+        n = cu[1] - cu[0]
+        K = int(b.context_lens[0])
+        nblk = -(-K // b.block_size)
+        ids = b.block_table[0, :nblk].long()
+        row = np.arange(nblk, dtype=np.int32)[None, :]
+        pairs = n * (K - n + 1) + n * (n - 1) // 2
+        done, dt, heads = 0, 0.0, 0
+        while dt < args.cpu_budget and heads < b.num_heads:
+            h = heads
+            kc = to_numpy_bits(b.k_cache.index_select(0, ids)[:, h:h + 1])
+            vc = to_numpy_bits(b.v_cache.index_select(0, ids)[:, h:h + 1])
+            qn = to_numpy_bits(b.q[:n, h:h + 1])
+            c0 = time.perf_counter()
+            oracle.paged_prefill(qn, kc, vc, row, np.array([0, n], dtype=np.int32),
+                                 np.array([K], dtype=np.int32), b.scale, 1, b.block_size,
+                                 "f16", "f16")
+            dt += time.perf_counter() - c0
+            done += 4 * b.head_size * pairs
+            heads += 1
+        import threadpoolctl
+        cores = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+        cpu = {"value": done / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": f"sequence 0 ({n} queries over {K} keys), {heads} of "
+                         f"{b.num_heads} heads, fp64 numpy, {dt:.1f} s"}
+    return {
+        "metric": "chunked prefill query tokens/s and achieved TFLOP/s (% of f16 MFMA peak), 1×MI355X",
+        "value": T / (ms * 1e-3), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "llama7b_prefill_chunks: 16 seqs x 512-token chunks after "
+                               "U{0..1536} cached tokens, 32 = 32 kv heads, head 128, block 16, f16",
+                   "total_query_tokens": T, "step": "pa_cache_write + pa_prefill"},
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill", "achieved": achieved,
+                     "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_MFMA_F16_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "kernel_ms": kern_ms,
+                     "kernel_sources": kernel_source_hash()},
+        "cpu_baseline": cpu,
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,9 +338,11 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama7b_mha",
                     choices=["worked_example", "llama7b_mha", "gqa", "long_context",
                              "fp8_shared_prefix"])
-    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap_out", "swap_in"],
+    ap.add_argument("--op", default="step",
+                    choices=["step", "copy_blocks", "swap_out", "swap_in", "prefill"],
                     help="step: one decode step (default); copy_blocks: copy-on-write copies "
-                         "inside a pool; swap_out / swap_in: blocks to / from a pinned host pool")
+                         "inside a pool; swap_out / swap_in: blocks to / from a pinned host "
+                         "pool; prefill: one chunked-prefill step (cache write + pa_prefill)")
     ap.add_argument("--unfused", action="store_true",
                     help="one-pass workloads: pa_cache_write then pa_decode instead of the "
                          "single pa_decode_append launch")
@@ -268,6 +370,9 @@ def main(argv=None):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.op == "prefill":
+        print(json.dumps(bench_prefill(args, torch, pa, dev)))
+        return 0
     if args.op != "step":
         print(json.dumps(bench_block_copy(args, torch, pa, dev)))
         return 0
