@@ -18,6 +18,7 @@ copies a hand-checked copy plus copy-on-write and swap scenarios whose
 attention is known.  No function
 here is "parity unpinned".
 """
+from .block_manager import BlockManager, NoFreeBlocks  # noqa: F401
 from .block_ops import copy_blocks, cow_step  # noqa: F401
 from .formats import (  # noqa: F401
     E4M3_MAX,

@@ -229,3 +229,33 @@ def test_prefill_off_by_one_mask_is_caught(monkeypatch):
     monkeypatch.setattr(pa_oracle, "paged_prefill", bad)
     monkeypatch.setattr(oracle, "paged_prefill", bad)
     assert _fails([t_pf.test_brute_force_tiny, lambda: t_pf.test_sdpa_with_explicit_mask(True)])
+
+
+def test_block_manager_lifo_free_list_is_caught(monkeypatch):
+    import oracle.block_manager as bmod
+    import test_oracle_block_manager as t_bm
+
+    def release_front(self, b):
+        self.refs[b] -= 1
+        if self.refs[b] == 0:
+            del self.refs[b]
+            self.free.insert(0, b)                   # freed blocks reused first
+    monkeypatch.setattr(bmod._Pool, "release", release_front)
+    assert _fails([t_bm.test_allocation_from_the_front_and_release_to_the_back,
+                   t_bm.test_swap_out_and_in])
+
+
+def test_block_manager_without_copy_on_write_is_caught(monkeypatch):
+    import oracle.block_manager as bmod
+    import test_oracle_block_manager as t_bm
+
+    def append_in_place(self, sid):
+        st = self.seqs[sid]
+        pos = st["len"]
+        j = pos // self.bs
+        if j == len(st["blocks"]):
+            st["blocks"].append(self.gpu.take(1)[0])
+        st["len"] = pos + 1
+        return st["blocks"][j] * self.bs + pos % self.bs, None
+    monkeypatch.setattr(bmod.BlockManager, "append_slot", append_in_place)
+    assert _fails([t_bm.test_fork_shares_and_copy_on_write_splits])
