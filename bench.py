@@ -230,6 +230,97 @@ def bench_block_copy(args, torch, pa, dev):
     }
 
 
+def bench_fragmentation(args, pa):
+    """The simulation the how-it-works page proposes (its closing project):
+    100 requests with lengths uniform in [50, 500] tokens, block size 16,
+    against reserving max_len = 512 contiguous slots per request.  The paged
+    side runs through the library's block manager, which grows every
+    sequence token by token (append_slots, as decode steps do).  Reported:
+    the share of allocated slots left unused by both schemes, how many such
+    requests fit in the memory of 100 reserved ones, and the manager's
+    append rate through its Python binding, one call per decode step of the
+    live requests (the oracle's Python manager is the baseline)."""
+    import random
+    import numpy as np
+    BS, MAXLEN, N = 16, 512, 100
+    rng = random.Random(7)
+    lens = [rng.randint(50, 500) for _ in range(N)]
+    pool_slots = N * MAXLEN                          # the memory of 100 reserved requests
+    bm = pa.BlockManager(pool_slots // BS, 0, BS)
+    for i, L in enumerate(lens):                     # prompt of half the length, then decode
+        bm.add_sequence(i, L // 2)
+    t_append = 0.0
+    appended = 0
+    cur = [L // 2 for L in lens]
+    live = list(range(N))
+    while live:
+        t0 = time.perf_counter()
+        slots, _ = bm.append_slots(live)             # one decode step of the live requests
+        t_append += time.perf_counter() - t0
+        appended += len(live)
+        for i in live:
+            cur[i] += 1
+        live = [i for i in live if cur[i] < lens[i]]
+    assert all(bm.seq_len(i) == lens[i] for i in range(N))
+    used_blocks = pool_slots // BS - bm.num_free()
+    paged_frag = 1.0 - sum(lens) / (used_blocks * BS)
+    naive_frag = 1.0 - sum(lens) / (N * MAXLEN)
+    # how many requests of the same length distribution fit in the same memory
+    fit, i = 0, N
+    while True:
+        L = rng.randint(50, 500)
+        try:
+            bm.add_sequence(i, L)
+        except pa.BlockManager.NoFreeBlocks:
+            break
+        fit += 1
+        i += 1
+    paged_concurrency = N + fit
+    # serving-sized batch: 4096 live sequences, 100 decode steps
+    big = pa.BlockManager(1 << 20, 0, BS)
+    ids = list(range(4096))
+    for j in ids:
+        big.add_sequence(j, 100)
+    t0 = time.perf_counter()
+    for _ in range(100):
+        big.append_slots(ids)
+    big_rate = 4096 * 100 / (time.perf_counter() - t0)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        ob = oracle.BlockManager(pool_slots // BS, 0, BS)
+        for j, L in enumerate(lens):
+            ob.add_sequence(j, L // 2)
+        dt, done = 0.0, 0
+        cur = [L // 2 for L in lens]
+        live = list(range(N))
+        while live:
+            c0 = time.perf_counter()
+            for j in live:
+                ob.append_slot(j)
+            dt += time.perf_counter() - c0
+            done += len(live)
+            for j in live:
+                cur[j] += 1
+            live = [j for j in live if cur[j] < lens[j]]
+        cpu = {"value": done / dt, "unit": "slots/s", "cores": 1, "kind": "oracle",
+               "sample": f"the same {done} appends through the oracle's Python manager, {dt:.2f} s"}
+    return {
+        "metric": "paged KV cache: unused share of allocated slots (%), how-it-works simulation",
+        "value": 100.0 * paged_frag, "unit": "%", "n_gpus": 0, "steps": 1, "warmup": 0,
+        "ms_per_step": t_append * 1e3, "higher_is_better": False, "scaling": "none",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "100 requests, lengths U[50,500], prompt = half, the rest "
+                               "generated token by token; block 16 vs 512 reserved per request",
+                   "naive_unused_percent": 100.0 * naive_frag,
+                   "requests_in_the_memory_of_100_reserved": paged_concurrency,
+                   "concurrency_ratio": paged_concurrency / N,
+                   "manager_append_rate_slots_per_s": appended / t_append,
+                   "manager_append_rate_4096_seq_batches_slots_per_s": big_rate},
+        "roofline": None, "cpu_baseline": cpu,
+    }
+
+
 PEAK_MFMA_F16_TFLOPS = 2500.0
 
 
@@ -339,10 +430,13 @@ def main(argv=None):
                     choices=["worked_example", "llama7b_mha", "gqa", "long_context",
                              "fp8_shared_prefix"])
     ap.add_argument("--op", default="step",
-                    choices=["step", "copy_blocks", "swap_out", "swap_in", "prefill"],
+                    choices=["step", "copy_blocks", "swap_out", "swap_in", "prefill",
+                             "fragmentation"],
                     help="step: one decode step (default); copy_blocks: copy-on-write copies "
                          "inside a pool; swap_out / swap_in: blocks to / from a pinned host "
-                         "pool; prefill: one chunked-prefill step (cache write + pa_prefill)")
+                         "pool; prefill: one chunked-prefill step (cache write + pa_prefill); "
+                         "fragmentation: the host block manager on the how-it-works page's "
+                         "100-request simulation (CPU only)")
     ap.add_argument("--unfused", action="store_true",
                     help="one-pass workloads: pa_cache_write then pa_decode instead of the "
                          "single pa_decode_append launch")
@@ -360,6 +454,9 @@ def main(argv=None):
 
     import torch
     import paged_kv_cache_78_amd as pa
+    if args.op == "fragmentation":
+        print(json.dumps(bench_fragmentation(args, pa)))
+        return 0
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (ROCm) and the built libpa.so")
     pa.lib()

@@ -82,7 +82,10 @@ typedef enum {
   PA_ERR_DTYPE = -4,       /* element type combination not supported        */
   PA_ERR_WORKSPACE = -5,   /* partition size or workspace invalid           */
   PA_ERR_HIP = -6,         /* the HIP runtime refused the launch            */
-  PA_ERR_MEMORY = -7       /* a pool is not device-accessible memory        */
+  PA_ERR_MEMORY = -7,      /* a pool is not device-accessible memory        */
+  PA_ERR_NO_BLOCKS = -8,   /* block manager: not enough free blocks         */
+  PA_ERR_SEQUENCE = -9     /* block manager: unknown, duplicate or swapped-
+                              out sequence for this call                    */
 } pa_status;
 
 /* Static text for a status code (never NULL). */
@@ -272,6 +275,67 @@ int pa_reduce(void* out, const float* tmp_out, const float* max_logits,
               const float* exp_sums, const int32_t* context_lens, int32_t num_seqs,
               int32_t num_heads, int32_t head_size, int32_t partition_size,
               int32_t max_num_partitions, pa_dtype out_dtype, void* stream);
+
+/*
+ * Host block manager (CPU code; no GPU call, no stream).  It decides where
+ * every token's K/V lives: the block tables, slot_mapping and block copies
+ * the kernels above consume.  "How does paged attention work (in detail)",
+ * sections 2-4: free blocks wait in a FIFO queue (taken from its front,
+ * freed blocks join its back in table order), each block counts its
+ * references, a sequence gets a new block only when a token starts an
+ * unmapped logical block, a token landing in a shared block first gets the
+ * writer its own copy (copy-on-write), and a preempted sequence's blocks
+ * move to a CPU pool and back (section 4.3; vLLM paper summary, section 5).
+ * Every call either succeeds or changes nothing.  A manager is not
+ * thread-safe.  Block ids are int32; num_gpu_blocks * block_size must fit
+ * int32 (slots do).
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* New manager with empty sequences; gpu_free_order (num_gpu_blocks distinct
+ * ids, or NULL for 0, 1, ...) is the initial free queue.  NULL on invalid
+ * sizes or allocation failure. */
+pa_block_manager* pa_bm_create(int32_t num_gpu_blocks, int32_t num_cpu_blocks,
+                               int32_t block_size, const int32_t* gpu_free_order);
+void pa_bm_destroy(pa_block_manager* m);
+
+/* A new sequence holding num_tokens tokens: ceil(num_tokens / block_size)
+ * blocks.  PA_ERR_SEQUENCE if seq_id exists, PA_ERR_NO_BLOCKS if short. */
+int pa_bm_add_sequence(pa_block_manager* m, int64_t seq_id, int64_t num_tokens);
+
+/* child shares every block of parent (parallel sampling, beam search). */
+int pa_bm_fork(pa_block_manager* m, int64_t parent, int64_t child);
+
+/* Slot of the sequence's next token (its length grows by one).  copy_pair
+ * [2] receives (src, dst) when the token lands in a shared block and the
+ * caller must copy src to dst (pa_copy_blocks) before writing, else -1. */
+int pa_bm_append_slot(pa_block_manager* m, int64_t seq_id, int32_t* slot, int32_t* copy_pair);
+
+/* pa_bm_append_slot for n distinct sequences at once: slots [n] (a decode
+ * step's slot_mapping), copy_pairs [n][2] of which *num_copies are used. */
+int pa_bm_append_slots(pa_block_manager* m, const int64_t* seq_ids, int32_t n, int32_t* slots,
+                       int32_t* copy_pairs, int32_t* num_copies);
+
+/* Drop a sequence; blocks whose count reaches zero return to the queue. */
+int pa_bm_free(pa_block_manager* m, int64_t seq_id);
+
+/* Move a sequence's blocks to the CPU pool (swap_out) or back (swap_in):
+ * pairs [k][2] = (from, to) in table order, the copies to perform with
+ * pa_copy_blocks before the freed blocks are reused.  A shared GPU block
+ * stays for its other users.  max_pairs bounds k (PA_ERR_SHAPE if short). */
+int pa_bm_swap_out(pa_block_manager* m, int64_t seq_id, int32_t* pairs, int32_t max_pairs,
+                   int32_t* num_pairs);
+int pa_bm_swap_in(pa_block_manager* m, int64_t seq_id, int32_t* pairs, int32_t max_pairs,
+                  int32_t* num_pairs);
+
+/* Block tables [n][max_blocks] (padded with -1) and lengths [n] (may be
+ * NULL) of n sequences: a batch's block_table and context_lens. */
+int pa_bm_block_tables(const pa_block_manager* m, const int64_t* seq_ids, int32_t n,
+                       int32_t* tables, int32_t max_blocks, int64_t* lens);
+
+int64_t pa_bm_seq_len(const pa_block_manager* m, int64_t seq_id);            /* -1: unknown */
+int32_t pa_bm_num_free(const pa_block_manager* m, int32_t on_gpu);
+int32_t pa_bm_ref_count(const pa_block_manager* m, int32_t block, int32_t on_gpu);
 
 #ifdef __cplusplus
 }

@@ -2,6 +2,7 @@
 Python binding.  See include/pa.h for the ABI."""
 from .binding import (  # noqa: F401
     EXPORTS,
+    BlockManager,
     PagedAttentionError,
     cache_write,
     copy_blocks,

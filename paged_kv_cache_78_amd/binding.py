@@ -21,7 +21,10 @@ _DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_F
 
 EXPORTS = ("pa_status_string", "pa_abi_version", "pa_cache_write", "pa_decode",
            "pa_decode_append", "pa_prefill", "pa_copy_blocks", "pa_partition_workspace_bytes",
-           "pa_decode_partitioned", "pa_reduce")
+           "pa_decode_partitioned", "pa_reduce", "pa_bm_create", "pa_bm_destroy",
+           "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_append_slot", "pa_bm_append_slots",
+           "pa_bm_free", "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_block_tables",
+           "pa_bm_seq_len", "pa_bm_num_free", "pa_bm_ref_count")
 
 
 class PagedAttentionError(RuntimeError):
@@ -65,6 +68,27 @@ def lib() -> ctypes.CDLL:
                                         vp, vp, vp, vp]
     L.pa_reduce.restype = ctypes.c_int
     L.pa_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    P = ctypes.POINTER
+    pi32, pi64 = P(i32), P(i64)
+    L.pa_bm_create.restype = vp
+    L.pa_bm_create.argtypes = [i32, i32, i32, pi32]
+    L.pa_bm_destroy.restype = None
+    L.pa_bm_destroy.argtypes = [vp]
+    for name, args in (("pa_bm_add_sequence", [vp, i64, i64]), ("pa_bm_fork", [vp, i64, i64]),
+                       ("pa_bm_append_slot", [vp, i64, pi32, pi32]),
+                       ("pa_bm_append_slots", [vp, pi64, i32, pi32, pi32, pi32]),
+                       ("pa_bm_free", [vp, i64]),
+                       ("pa_bm_swap_out", [vp, i64, pi32, i32, pi32]),
+                       ("pa_bm_swap_in", [vp, i64, pi32, i32, pi32]),
+                       ("pa_bm_block_tables", [vp, pi64, i32, pi32, i32, pi64])):
+        getattr(L, name).restype = ctypes.c_int
+        getattr(L, name).argtypes = args
+    L.pa_bm_seq_len.restype = i64
+    L.pa_bm_seq_len.argtypes = [vp, i64]
+    L.pa_bm_num_free.restype = i32
+    L.pa_bm_num_free.argtypes = [vp, i32]
+    L.pa_bm_ref_count.restype = i32
+    L.pa_bm_ref_count.argtypes = [vp, i32, i32]
     _lib = L
     return L
 
@@ -291,3 +315,109 @@ def decode_partitioned(q, k_cache, v_cache, block_table, context_lens, scale,
     decode_partitioned_only(q, k_cache, v_cache, block_table, context_lens, scale, partition_size,
                             max_context_len, workspace, k_scale, v_scale, stream)
     return reduce(out, workspace, context_lens, partition_size, stream)
+
+
+# ----------------------------------------------------------------------------
+# host block manager (CPU; no GPU call)
+
+class BlockManager:
+    """The library's host block manager (pa_bm_*): block tables, slots and
+    the block copies a decode step needs.  Raises PagedAttentionError on a
+    failed call; NoFreeBlocks when the pool is short."""
+
+    class NoFreeBlocks(PagedAttentionError):
+        pass
+
+    def __init__(self, num_gpu_blocks: int, num_cpu_blocks: int, block_size: int,
+                 gpu_free_order=None):
+        L = lib()
+        order = None
+        if gpu_free_order is not None:
+            arr = (ctypes.c_int32 * len(gpu_free_order))(*[int(b) for b in gpu_free_order])
+            order = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+        self._h = L.pa_bm_create(num_gpu_blocks, num_cpu_blocks, block_size, order)
+        if not self._h:
+            raise PagedAttentionError("pa_bm_create: invalid sizes or free order")
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            lib().pa_bm_destroy(h)
+            self._h = None
+
+    def _ok(self, st, what):
+        if st == -8:
+            raise BlockManager.NoFreeBlocks(f"{what}: not enough free blocks")
+        _check(st, what)
+
+    def add_sequence(self, seq_id: int, num_tokens: int):
+        self._ok(lib().pa_bm_add_sequence(self._h, seq_id, num_tokens), "pa_bm_add_sequence")
+
+    def fork(self, parent: int, child: int):
+        self._ok(lib().pa_bm_fork(self._h, parent, child), "pa_bm_fork")
+
+    def append_slot(self, seq_id: int):
+        slot = ctypes.c_int32()
+        pair = (ctypes.c_int32 * 2)()
+        self._ok(lib().pa_bm_append_slot(self._h, seq_id, ctypes.byref(slot), pair),
+                 "pa_bm_append_slot")
+        return slot.value, (None if pair[0] < 0 else (pair[0], pair[1]))
+
+    def append_slots(self, seq_ids):
+        """slots [n] (int32 tensor) and copy pairs [k, 2] (int32 tensor) of one
+        decode step over the listed sequences."""
+        n = len(seq_ids)
+        ids = (ctypes.c_int64 * max(n, 1))(*[int(s) for s in seq_ids])
+        slots = torch.empty(n, dtype=torch.int32)
+        pairs = torch.empty((max(n, 1), 2), dtype=torch.int32)
+        nc = ctypes.c_int32()
+        self._ok(lib().pa_bm_append_slots(
+            self._h, ids, n, ctypes.cast(slots.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+            ctypes.cast(pairs.data_ptr(), ctypes.POINTER(ctypes.c_int32)), ctypes.byref(nc)),
+            "pa_bm_append_slots")
+        return slots, pairs[:nc.value].clone()
+
+    def free(self, seq_id: int):
+        self._ok(lib().pa_bm_free(self._h, seq_id), "pa_bm_free")
+
+    def _move(self, fn, seq_id, what):
+        k = max(1, (self.seq_len(seq_id) + self.block_size - 1) // self.block_size)
+        pairs = (ctypes.c_int32 * (2 * k))()
+        n = ctypes.c_int32()
+        self._ok(fn(self._h, seq_id, pairs, k, ctypes.byref(n)), what)
+        return [(pairs[2 * i], pairs[2 * i + 1]) for i in range(n.value)]
+
+    def swap_out(self, seq_id: int):
+        return self._move(lib().pa_bm_swap_out, seq_id, "pa_bm_swap_out")
+
+    def swap_in(self, seq_id: int):
+        return self._move(lib().pa_bm_swap_in, seq_id, "pa_bm_swap_in")
+
+    def block_tables(self, seq_ids, max_blocks: int):
+        """(block_table [n, max_blocks] int32 padded with -1, lengths [n] int64)."""
+        n = len(seq_ids)
+        ids = (ctypes.c_int64 * max(n, 1))(*[int(s) for s in seq_ids])
+        tables = torch.empty((n, max_blocks), dtype=torch.int32)
+        lens = torch.empty(n, dtype=torch.int64)
+        self._ok(lib().pa_bm_block_tables(
+            self._h, ids, n, ctypes.cast(tables.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+            max_blocks, ctypes.cast(lens.data_ptr(), ctypes.POINTER(ctypes.c_int64))),
+            "pa_bm_block_tables")
+        return tables, lens
+
+    def table(self, seq_id: int):
+        t, n = self.block_tables([seq_id], max(1, -(-self.seq_len(seq_id) // self.block_size)))
+        return [b for b in t[0].tolist() if b >= 0]
+
+    def seq_len(self, seq_id: int) -> int:
+        n = lib().pa_bm_seq_len(self._h, seq_id)
+        if n < 0:
+            raise PagedAttentionError(f"unknown sequence {seq_id}")
+        return n
+
+    def num_free(self, on_gpu: bool = True) -> int:
+        return lib().pa_bm_num_free(self._h, 1 if on_gpu else 0)
+
+    def ref_count(self, block: int, on_gpu: bool = True) -> int:
+        return lib().pa_bm_ref_count(self._h, block, 1 if on_gpu else 0)

@@ -2,8 +2,9 @@
 
     python -m paged_kv_cache_78_amd.build        # or build() from Python
 
-Each csrc/*.hip file is compiled to an object with hipcc, in parallel, and the
-objects are linked into paged_kv_cache_78_amd/libpa.so.  hipcc cross-compiles,
+Each csrc/*.hip file is compiled to an object with hipcc (csrc/*.cpp, host
+code only, with g++), in parallel, and the objects are linked into
+paged_kv_cache_78_amd/libpa.so.  hipcc cross-compiles,
 so this works on a machine without a GPU.
 """
 from __future__ import annotations
@@ -36,13 +37,21 @@ COMMON = [
 ]
 
 
+# host-only C++ (the block manager): the system C++ compiler
+HOST = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
+
+
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") or f.endswith(".cpp"))
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src)[:-4] + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", src, "-o", obj]
+    obj = os.path.join(OBJ, os.path.splitext(os.path.basename(src))[0] + ".o")
+    if src.endswith(".cpp"):
+        cmd = [shutil.which("g++") or "g++", *HOST, "-c", src, "-o", obj]
+    else:
+        cmd = [_hipcc(), *COMMON, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

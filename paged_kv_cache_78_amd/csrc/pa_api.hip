@@ -151,6 +151,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "invalid partition size or workspace";
     case PA_ERR_HIP: return "the HIP runtime refused the launch";
     case PA_ERR_MEMORY: return "a pointer is not device-accessible memory (device, managed or pinned host)";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PA_ERR_SEQUENCE: return "unknown, duplicate or swapped-out sequence for this call";
     default: return "unknown status";
   }
 }
