@@ -33,9 +33,10 @@ struct Mma<F16> {
   }
   static __device__ __forceinline__ float lo(uint32_t w) { return f16_lo(w); }
   static __device__ __forceinline__ float hi(uint32_t w) { return f16_hi(w); }
-  // two exactly representable floats (decoded fp8) -> packed pair
-  static __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  // e4m3fn bytes 0,1 (HI: 2,3) of w -> packed f16 pair (exact; scale 1)
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t fp8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
   }
 };
 
@@ -57,10 +58,9 @@ struct Mma<BF16> {
   }
   static __device__ __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
   static __device__ __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
-  static __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
-    // upper halves of the two binary32 patterns (exact for decoded e4m3fn)
-    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
-                                 0x07060302u);
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t fp8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   }
 };
 

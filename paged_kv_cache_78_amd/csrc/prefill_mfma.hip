@@ -189,10 +189,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_kernel(const 
       const u32x4_t w = kd[c >> 1];
       const uint32_t a = (c & 1) ? w[2] : w[0];
       const uint32_t b = (c & 1) ? w[3] : w[1];
-      const float2_t a0 = fp8x2_to_f32<false>(a), a1 = fp8x2_to_f32<true>(a);
-      const float2_t b0 = fp8x2_to_f32<false>(b), b1 = fp8x2_to_f32<true>(b);
-      return u32x4_t{M::pack_exact(a0[0], a0[1]), M::pack_exact(a1[0], a1[1]),
-                     M::pack_exact(b0[0], b0[1]), M::pack_exact(b1[0], b1[1])};
+      return u32x4_t{M::template fp8x2<false>(a), M::template fp8x2<true>(a),
+                     M::template fp8x2<false>(b), M::template fp8x2<true>(b)};
     }
   };
   auto v_operand = [&](const u32x4_t& w, int e) -> u32x2_t {
@@ -200,8 +198,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_kernel(const 
       return u32x2_t{w[2 * e], w[2 * e + 1]};
     } else {
       const uint32_t v = w[e];
-      const float2_t v0 = fp8x2_to_f32<false>(v), v1 = fp8x2_to_f32<true>(v);
-      return u32x2_t{MV::pack_exact(v0[0], v0[1]), MV::pack_exact(v1[0], v1[1])};
+      return u32x2_t{MV::template fp8x2<false>(v), MV::template fp8x2<true>(v)};
     }
   };
 
