@@ -11,8 +11,9 @@ pa_decode_partitioned + pa_reduce.  Prints one JSON line.
 
 value = KV tokens attended per second over the K timed steps (whole job).
 roofline = the attention kernel's algorithmic HBM bytes per launch (a block
-shared by several sequences counted once) / its mean launch time (HIP events
-on the launch stream), against 8 TB/s.
+shared by several sequences counted once) / its mean launch duration (HIP
+events on the launch stream: around the whole timed region when the step is
+that one launch, else around each launch), against 8 TB/s.
 cpu_baseline = the CPU oracle (test infrastructure, fp64 numpy) on a bounded
 sample of the same workload, timed on this host.
 """
@@ -490,7 +491,7 @@ def main(argv=None):
         if not fused:
             pa.cache_write(wl.new_k, wl.new_v, wl.k_cache, wl.v_cache, wl.slot_mapping,
                            k_scale=wl.k_scale, v_scale=wl.v_scale)
-        if record:
+        if record and not fused:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -504,7 +505,7 @@ def main(argv=None):
         else:
             pa.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, lens_step, wl.scale,
                       k_scale=wl.k_scale, v_scale=wl.v_scale, out=out)
-        if record:
+        if record and not fused:
             e1.record()
             ev.append((e0, e1))
         if partitioned:
@@ -513,16 +514,26 @@ def main(argv=None):
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
+    # the fused step is one launch: its average duration is the events around
+    # the whole timed region over the launches; a multi-launch step brackets
+    # each attention launch with its own pair
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    r0.record()
     for _ in range(args.steps):
         step(True)
+    r1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens = sum(lens_host)
     value = tokens / (ms_per_step * 1e-3)
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    if fused:
+        kern_ms = r0.elapsed_time(r1) / args.steps
+    else:
+        kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
     # roofline bytes count a shared block once (it is read from HBM once);
     # the logical count reads it once per sequence
     cached = wl.context_lens.cpu().tolist() if fused else lens_host
@@ -574,6 +585,8 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": alg,
             "logical_bytes_per_launch": alg_logical,
             "kernel_ms": kern_ms,
+            "kernel_timing": ("HIP events around the timed region (launches back to back)" if fused
+                              else "HIP events around each attention launch"),
             "kernel_sources": src_hash,
         },
         "cpu_baseline": cpu,

@@ -51,8 +51,12 @@ namespace {
 
 constexpr float kNegInf = kMfmaNegInf;
 
+// fp8 caches: three wavefronts per SIMD fit without spilling (16-bit caches
+// need the register budget of two), and the extra wavefronts keep more tiles
+// in flight per compute unit.
 template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void decode_mfma_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(CT::kBytes == 1 ? 3 : 1)))
+void decode_mfma_kernel(const DecodeParams p) {
   constexpr int ESZ = CT::kBytes;
   constexpr int SUB = BS / 16;              // 16-token sub-tiles per block
   constexpr int TILE_BYTES = BS * D * ESZ;
