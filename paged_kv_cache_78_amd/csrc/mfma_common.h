@@ -31,6 +31,16 @@ struct Mma<F16> {
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     return (uint32_t)to_f16_bits(lo) | ((uint32_t)to_f16_bits(hi) << 16);
   }
+  // the same as one v_cvt_pk_f16_f32
+  static __device__ __forceinline__ uint32_t pack_pk(float lo, float hi) {
+    const half2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  // acc + the two 16-bit values of w (exact products, one fp32 sum)
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(as_half2(w), one, acc, false);
+  }
   static __device__ __forceinline__ float lo(uint32_t w) { return f16_lo(w); }
   static __device__ __forceinline__ float hi(uint32_t w) { return f16_hi(w); }
   // e4m3fn bytes 0,1 (HI: 2,3) of w -> packed f16 pair (exact; scale 1)
@@ -56,8 +66,13 @@ struct Mma<BF16> {
     r[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, r);
   }
+  static __device__ __forceinline__ uint32_t pack_pk(float lo, float hi) { return pack(lo, hi); }
   static __device__ __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
   static __device__ __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    const bf162_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(as_bf162(w), one, acc, false);
+  }
   template <bool HI>
   static __device__ __forceinline__ uint32_t fp8x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));

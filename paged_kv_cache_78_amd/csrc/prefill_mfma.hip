@@ -10,20 +10,34 @@
 // K_s - n_s + i and, causal, attends keys 0 .. K_s - n_s + i.
 //
 // Layout of the work: the n_s * G query rows of (sequence, kv head) (G query
-// heads per kv head, row r = token r / G, head r % G) are cut into blocks of
-// 16 rows.  A wavefront owns one block: the 16 rows are the 16 columns of
+// heads per kv head, row r = token r / G, head r % G) are cut into workgroup
+// chunks of ROWS = 4 wavefronts x R blocks of 16 rows.  A workgroup walks the
+// keys in stages of 32 (two 16-key sub-tiles): its 256 threads copy the
+// stage's K and V tiles (gathered through the block table) into LDS once, and
+// every wavefront multiplies them with its R row blocks:
 //
-//   S^T [16 tokens x 16 rows] = K [16 x D] . Q^T [D x 16]      (v_mfma 16x16x32)
-//   O^T [D x 16 rows]        += V^T [D x 16] . P^T [16 x 16]   (v_mfma 16x16x16)
+//   S^T [16 keys x 16 rows] = K [16 x D] . Q^T [D x 16]        (v_mfma 16x16x32)
+//   O^T [16 dims x 16 rows] += V^T [16 x 32 keys] . P^T [32 x 16]  (v_mfma 16x16x32)
 //
-// exactly as in the decode kernel for a group of heads, with one online
-// softmax per column and a per-column causal limit.  The wavefront streams
-// the key tiles up to the largest limit of its columns through the block
-// table; four wavefronts (64 rows) share a workgroup, so a tile they all read
-// comes from the same L2 lines.  Weight precision, fp8 decoding and masking
-// follow the decode kernel: P in f16 (f16 and fp8 caches) or split into two
-// bf16 parts (bf16 caches); keys past a column's limit get a -inf logit and
-// a zero weight, and V rows past the context are zeroed before the product.
+// so each K/V byte read from memory feeds 16 * 4 * R query rows, and each
+// operand read from LDS feeds R products.  Lane (n, g) holds column n (one
+// query row) and rows 4g..4g+3 of every S^T and O^T product, so a row's
+// softmax state lives in the lanes of its column.  In the PV product the
+// 8 contraction elements of lane group g are the keys 4g..4g+3 of both
+// sub-tiles, which is where S^T put them: the weights go into the B operand
+// without any exchange, and the V operand reads the matching token quads.
+// LDS rows are padded (K by 16 bytes per key, V by 128 bytes per token quad)
+// so that the operand reads hit every bank once.
+//
+// Work mapping: workgroups go to the XCDs round robin, so the chunks of one
+// (sequence, kv head) are given workgroup indices that land on the same XCD
+// and share its L2; causal chunks with more keys go first.
+//
+// Weight precision, fp8 decoding and masking follow the decode kernels: P in
+// f16 (f16 and fp8 caches) or split into two bf16 parts (bf16 caches); keys
+// past a row's limit get a -inf logit and weight 0, V elements of tokens past
+// the context are zeroed before the product (a NaN in an unused slot must not
+// reach it), and table entries past the context are never read.
 #include <type_traits>
 
 #include "mfma_common.h"
@@ -33,37 +47,90 @@
 namespace pa {
 namespace {
 
-constexpr int kPrefillWaves = 4;
-constexpr int kRowsPerWg = 16 * kPrefillWaves;
-constexpr int kPrefillNbuf = 3;
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfKeys = 32;           // keys per stage
+constexpr int kXcds = 8;              // workgroups go to the XCDs round robin
 constexpr float kNegInfP = kMfmaNegInf;
 constexpr float kSlackP = 8.0f;
+// s_waitcnt immediates (gfx9-family encoding): vmcnt(0) with expcnt and
+// lgkmcnt at their maxima (or in a vmcnt(n)), and lgkmcnt(0) alone
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
 
-template <typename QT, typename CT, int D, int BS, bool CAUSAL>
-__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_kernel(const PrefillParams p) {
-  constexpr int ESZ = CT::kBytes;
-  constexpr int SUB = BS / 16;
-  constexpr int TILE_BYTES = BS * D * ESZ;
-  constexpr int NQK = D / 32;
-  constexpr int NPV = D / 16;
-  constexpr int E = 16 / (4 * ESZ);
-  constexpr int NVL = NPV / E;
-  constexpr int NKL = ESZ == 2 ? NQK : NQK / 2;
-  constexpr int NBUF = kPrefillNbuf;
+// The block table through the constant address space: entries come in
+// through scalar loads, whose waits do not hold back the vector loads.
+typedef const __attribute__((address_space(4))) int32_t ConstTable;
+typedef __attribute__((address_space(3))) u32x2_t LdsU32x2;
+
+template <typename QT, typename CT, int D, int BS, int R>
+struct PfShape {
+  static constexpr int ESZ = CT::kBytes;
+  static constexpr int NQK = D / 32;                 // QK products per sub-tile
+  static constexpr int NPV = D / 16;                 // PV products per stage
+  static constexpr int ROWB = D * ESZ;               // bytes of one key's K row
+  static constexpr int GPR = ROWB / 16;              // 16-byte granules per K row
+  static constexpr int KB = kPfKeys * ROWB;          // K bytes of a stage (= V bytes)
+  static constexpr int NREG = KB / 1024;             // 1 KiB copy regions of K (and of V)
+  static constexpr int KPR = 1024 / ROWB;            // keys per K region
+  static constexpr int QB = 4 * ROWB;                // bytes of one token quad of V
+  static constexpr int QPR = 1024 / QB;              // token quads per V region
+  // one quad per region: pad regions by 128 bytes so that the quads read by
+  // lane groups 0 and 1 fall in different banks
+  static constexpr int VREG = 1024 + (QPR == 1 ? 128 : 0);
+  static constexpr int STAGE = KB + NREG * VREG;
+  static constexpr int NREGW = 2 * NREG / kPfWaves;  // copy regions per wavefront per stage
+  static constexpr int ROWS = kPfWaves * 16 * R;     // query rows per workgroup
+  static constexpr int TILE_BYTES = BS * D * ESZ;
+  static_assert(NREGW >= 1 && 2 * NREG % kPfWaves == 0 && NREGW <= 15, "stage split");
+  static_assert(kPfKeys % BS == 0, "a stage holds whole blocks");
+};
+
+// maximum of 8 values (NaN-propagating v_maximum3_f32, which needs no
+// canonicalised operands)
+__device__ __forceinline__ float max8(const float (&v)[8]) {
+  const float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]), v[2]);
+  const float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[3], v[4]), v[5]);
+  const float c = __builtin_elementwise_maximum(v[6], v[7]);
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+template <typename QT, typename CT, int D, int BS, bool CAUSAL, int R>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(const PrefillParams p,
+                                                                   int chunks) {
+  using Sh = PfShape<QT, CT, D, BS, R>;
+  constexpr int ESZ = Sh::ESZ, NQK = Sh::NQK, NPV = Sh::NPV;
+  constexpr int ROWB = Sh::ROWB, GPR = Sh::GPR, KB = Sh::KB, NREG = Sh::NREG, KPR = Sh::KPR;
+  constexpr int QB = Sh::QB, QPR = Sh::QPR, VREG = Sh::VREG, STAGE = Sh::STAGE;
+  constexpr int NREGW = Sh::NREGW, ROWS = Sh::ROWS, TILE_BYTES = Sh::TILE_BYTES;
+  constexpr int BPS = kPfKeys / BS;   // blocks per stage
+  constexpr int NST = 3;              // LDS ring: two stages in flight while one computes
   using M = Mma<QT>;
   using MV = std::conditional_t<ESZ == 1, Mma<F16>, Mma<QT>>;
   constexpr bool kSplitP = ESZ == 2 && __is_same(QT, BF16);
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15;          // query row (column of the products)
+  __shared__ __attribute__((aligned(16))) char s_kv[NST][STAGE];
+  __shared__ __attribute__((aligned(16))) int32_t s_ent[2][64];   // table windows
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 15;          // query row of the wavefront's row blocks
   const int g = lane >> 4;          // lane group
-  const int s = blockIdx.y;
-  const int kvh = blockIdx.z;
   const int H = p.num_heads;
   const int KVH = p.num_kv_heads;
   const int G = H / KVH;
   const int MB = p.max_blocks_per_seq;
+
+  // workgroup b runs on XCD b % 8: the chunks of item it = j / chunks * 8 +
+  // b % 8 (j = b / 8) all run on that XCD, the chunk with the most keys first
+  const int b = blockIdx.x;
+  const int j = b / kXcds;
+  const int item = (j / chunks) * kXcds + b % kXcds;
+  if (item >= p.num_seqs * KVH) return;
+  const int c = chunks - 1 - j % chunks;
+  const int s = item / KVH;
+  const int kvh = item % KVH;
 
   const int32_t q0 = p.cu_seqlens_q[s];
   const int32_t q1 = p.cu_seqlens_q[s + 1];
@@ -71,236 +138,455 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_kernel(const 
   // packed rows outside [0, total_q) are never touched
   if (q0 < 0 || q1 > p.total_q || nq <= 0) return;
   const int rows = nq * G;
-  if ((int)blockIdx.x * kRowsPerWg >= rows) return;
-  const int row = (int)blockIdx.x * kRowsPerWg + wave * 16 + n;
-  const bool row_ok = row < rows;
-  const int qi = row_ok ? row / G : 0;             // query token within the chunk
-  const int h = kvh * G + (row_ok ? row % G : 0);
+  const int row0 = c * ROWS;
+  if (row0 >= rows) return;
   const int K = p.context_lens[s];
   const bool bad_len = K < 0 || K > MB * BS || nq > p.max_seqlen_q;
-  // keys this row attends: positions 0 .. lim-1
-  int lim = 0;
-  if (row_ok && !bad_len) lim = CAUSAL ? min(K, K - nq + qi + 1) : K;
-  lim = max(lim, 0);
-  int wl = lim;                                     // the wavefront's largest limit
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) wl = max(wl, __shfl_xor(wl, o, 64));
-  const int ntiles = __builtin_amdgcn_readfirstlane((wl + BS - 1) / BS);
-  const int last_tile = (K + BS - 1) / BS - 1;      // the sequence's last (partial) tile
-  const int last_len = K - last_tile * BS;
 
-  auto write_out = [&](const float4_t (&o)[NPV]) {
-    if (!row_ok) return;
-    uint16_t* dst0 = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)(q0 + qi) * H + h) * D;
+  // this lane's rows (one per row block) and the keys each attends: 0 .. lim-1
+  int qi[R], hh[R], lim[R];
+  bool ok_row[R];
 #pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      float run[4 * E];
+  for (int r = 0; r < R; ++r) {
+    const int row = row0 + wave * 16 * R + 16 * r + n;
+    ok_row[r] = row < rows;
+    qi[r] = ok_row[r] ? row / G : 0;
+    hh[r] = kvh * G + (ok_row[r] ? row % G : 0);
+    int lm = 0;
+    if (ok_row[r] && !bad_len) lm = CAUSAL ? min(K, K - nq + qi[r] + 1) : K;
+    lim[r] = max(lm, 0);
+  }
+  // the workgroup's stages: up to its last row's limit (limits grow with the row)
+  int wg_lim = 0;
+  if (!bad_len) {
+    const int last_q = (min(row0 + ROWS, rows) - 1) / G;
+    wg_lim = max(CAUSAL ? min(K, K - nq + last_q + 1) : K, 0);
+  }
+  const int nstages = (wg_lim + kPfKeys - 1) / kPfKeys;
+  const int ctx_blocks = (K + BS - 1) / BS;           // table entries that may be read
+
+  auto store_rows = [&](const float4_t (&o)[R][NPV]) {
 #pragma unroll
-      for (int e = 0; e < E; ++e)
+    for (int r = 0; r < R; ++r) {
+      if (!ok_row[r]) continue;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)(q0 + qi[r]) * H + hh[r]) * D;
+      // lane (n, g) holds dims 16 jj + 4g .. +3 of product jj
 #pragma unroll
-        for (int r = 0; r < 4; ++r) run[E * r + e] = o[E * i + e][r];
-      uint16_t* dst = dst0 + 16 * E * i + 4 * E * g;
-#pragma unroll
-      for (int c = 0; c < E / 2; ++c) {
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          w[k] = (uint32_t)to_bits16<QT>(run[8 * c + 2 * k]) |
-                 ((uint32_t)to_bits16<QT>(run[8 * c + 2 * k + 1]) << 16);
-        *reinterpret_cast<u32x4_t*>(dst + 8 * c) = u32x4_t{w[0], w[1], w[2], w[3]};
+      for (int jj = 0; jj < NPV; ++jj) {
+        const uint32_t w0 = (uint32_t)to_bits16<QT>(o[r][jj][0]) |
+                            ((uint32_t)to_bits16<QT>(o[r][jj][1]) << 16);
+        const uint32_t w1 = (uint32_t)to_bits16<QT>(o[r][jj][2]) |
+                            ((uint32_t)to_bits16<QT>(o[r][jj][3]) << 16);
+        *reinterpret_cast<u32x2_t*>(dst + 16 * jj + 4 * g) = u32x2_t{w0, w1};
       }
     }
   };
 
   if (bad_len) {
-    float4_t o[NPV];
+    float4_t o[R][NPV];
     const float nanv = __builtin_nanf("");
 #pragma unroll
-    for (int j = 0; j < NPV; ++j) o[j] = float4_t{nanv, nanv, nanv, nanv};
-    write_out(o);
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int jj = 0; jj < NPV; ++jj) o[r][jj] = float4_t{nanv, nanv, nanv, nanv};
+    store_rows(o);
     return;
   }
 
-  // Q^T operand: row n's query token and head, dims in the QK chunk order
-  u32x4_t qb[NQK];
-  {
-    const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       ((int64_t)(q0 + qi) * p.q_token_stride + (int64_t)h * D) * 2;
+  // Q^T operands: row block r's column n, dims 32 cc + 8 g .. +7 of chunk cc
+  u32x4_t qb[R][NQK];
+
+  // ---- staging: the stage's K and V tiles, copied global -> LDS ----
+  // A copy instruction puts lane i's 16 bytes at LDS base + 16 i: each
+  // wavefront fills NREGW regions of 1 KiB per stage, wavefronts 0-1 those of
+  // K and 2-3 those of V.  K region r holds keys r*KPR .. with the 16-byte
+  // granules of key kk XOR-permuted by kk % GPR (so the 16 keys a K operand
+  // read touches land in different banks); V region r holds token quads
+  // r*QPR .. in the tile layout.
+  ConstTable* table = (ConstTable*)(p.block_table + (int64_t)s * MB);
+  const int32_t* table_v = p.block_table + (int64_t)s * MB;
+  const bool copies_k = wave < 2;
+  const char* cache = reinterpret_cast<const char*>(copies_k ? p.k_cache : p.v_cache) +
+                      (int64_t)kvh * TILE_BYTES;
+  const int64_t block_stride = (int64_t)KVH * TILE_BYTES;
+  const uint32_t nb32 = (uint32_t)min(p.num_blocks, (int64_t)INT32_MAX);
+  bool bad_entry = false;
+
+  // Every region lies in one cache block (KPR keys of K, QPR token quads of V,
+  // both dividing the block, and a stage starts on a block boundary), so its
+  // source is block address + a fixed offset + a per-lane offset, all but
+  // the block address fixed for the loop.
+  const int b16 = 16 * lane;
+  int rblk[NREGW], roff[NREGW], rdst[NREGW], loff[NREGW];
 #pragma unroll
-    for (int c = 0; c < NQK; ++c) {
-      qb[c] = row_ok ? *reinterpret_cast<const u32x4_t*>(qrow + qk_dim<ESZ>(c, g) * 2)
-                     : u32x4_t{0u, 0u, 0u, 0u};
+  for (int i = 0; i < NREGW; ++i) {
+    const int ri = wave * NREGW + i;
+    if (copies_k) {
+      const int k0 = ri * KPR;                          // first key of the region
+      const int kk = k0 + b16 / ROWB;
+      rblk[i] = k0 / BS;
+      roff[i] = (k0 % BS) * ROWB;
+      rdst[i] = ri * 1024;
+      loff[i] = (b16 / ROWB) * ROWB + (((b16 % ROWB) / 16) ^ (kk % GPR)) * 16;
+    } else {
+      const int vr = ri - NREG;
+      const int q0r = vr * QPR;                         // first token quad of the region
+      rblk[i] = (4 * q0r) / BS;
+      roff[i] = (q0r % (BS / 4)) * QB;
+      rdst[i] = KB + vr * VREG;
+      loff[i] = b16;
     }
   }
 
-  const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)kvh * TILE_BYTES;
-  const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE_BYTES;
-  const int64_t block_stride = (int64_t)KVH * TILE_BYTES;
-  TableWindow tw;
-  tw.init(p.block_table + (int64_t)s * MB, ntiles, p.num_blocks, lane);
-
-  uint32_t koff[SUB][NKL];
+  // copies stage t into the buffer at byte offset boff; e: the table entries
+  // of its blocks.  A block past the context or with a bad entry reads
+  // block 0 (any valid address: its keys are masked and its V elements
+  // zeroed).
+  auto stage_copy = [&](int t, int boff, const int (&e)[BPS]) {
+    const char* blk[BPS];
 #pragma unroll
-  for (int u = 0; u < SUB; ++u)
-#pragma unroll
-    for (int i = 0; i < NKL; ++i)
-      koff[u][i] = (uint32_t)((16 * u + n) * D * ESZ +
-                              (ESZ == 2 ? qk_dim<2>(i, g) * 2 : 64 * i + 16 * g));
-  uint32_t voff[SUB][NVL];
-#pragma unroll
-  for (int u = 0; u < SUB; ++u)
-#pragma unroll
-    for (int i = 0; i < NVL; ++i)
-      voff[u][i] = (uint32_t)(((4 * u + g) * D + E * (16 * i + n)) * 4 * ESZ);
-
-  u32x4_t kb[NBUF][SUB][NKL];
-  u32x4_t vb[NBUF][SUB][NVL];
-
-  auto issue = [&](u32x4_t (&kd)[SUB][NKL], u32x4_t (&vd)[SUB][NVL], int t) {
-    int phys = 0;
-    uint32_t bytes = 0;
-    if (t < ntiles) {
-      phys = tw.phys(t, lane);
-      bytes = TILE_BYTES;
-    }
-    const int64_t off = (int64_t)phys * block_stride;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, bytes);
-#pragma unroll
-    for (int u = 0; u < SUB; ++u)
-#pragma unroll
-      for (int i = 0; i < NKL; ++i) kd[u][i] = buffer_load16(rk, koff[u][i]);
-#pragma unroll
-    for (int u = 0; u < SUB; ++u)
-#pragma unroll
-      for (int i = 0; i < NVL; ++i) vd[u][i] = buffer_load16(rv, voff[u][i]);
-  };
-
-  float m = kNegInfP;
-  float l = 0.0f;
-  float4_t acc[NPV];
-#pragma unroll
-  for (int j = 0; j < NPV; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto k_operand = [&](const u32x4_t (&kd)[NKL], int c) -> u32x4_t {
-    if constexpr (ESZ == 2) {
-      return kd[c];
-    } else {
-      const u32x4_t w = kd[c >> 1];
-      const uint32_t a = (c & 1) ? w[2] : w[0];
-      const uint32_t b = (c & 1) ? w[3] : w[1];
-      return u32x4_t{M::template fp8x2<false>(a), M::template fp8x2<true>(a),
-                     M::template fp8x2<false>(b), M::template fp8x2<true>(b)};
-    }
-  };
-  auto v_operand = [&](const u32x4_t& w, int e) -> u32x2_t {
-    if constexpr (ESZ == 2) {
-      return u32x2_t{w[2 * e], w[2 * e + 1]};
-    } else {
-      const uint32_t v = w[e];
-      return u32x2_t{MV::template fp8x2<false>(v), MV::template fp8x2<true>(v)};
-    }
-  };
-
-  // tile t: keys t*BS + 16u + 4g + r for column n
-  auto process = [&](const u32x4_t (&kd)[SUB][NKL], const u32x4_t (&vd)[SUB][NVL], int t) {
-    const bool vmask = (t == last_tile) && (last_len < BS);   // V rows past the context
-    const bool kmask = (t + 1) * BS > lim;                    // some key past this column's limit
-#pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-      float4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NQK; ++c) sc = M::qk(k_operand(kd[u], c), qb[c], sc);
-      float x[4];
-      bool ok[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ok[r] = !kmask || (t * BS + 16 * u + 4 * g + r) < lim;
-        x[r] = ok[r] ? sc[r] * p.qk_scale_log2 : kNegInfP;
+    for (int bi = 0; bi < BPS; ++bi) {
+      uint32_t ph = (uint32_t)e[bi];
+      if (t * BPS + bi >= ctx_blocks) ph = 0;
+      else if (ph >= nb32) {                            // negative or past the pool
+        bad_entry = true;
+        ph = 0;
       }
-      float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (__builtin_amdgcn_ballot_w64(mt > m + kSlackP) != 0) {
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float mn = fmaxf(m, mt);
-        const float alpha = (m == mn) ? 1.0f : exp2_hw(m - mn);
-        m = mn;
-        l *= alpha;
+      blk[bi] = cache + (int64_t)ph * block_stride;
+    }
 #pragma unroll
-        for (int j = 0; j < NPV; ++j) acc[j] *= alpha;
+    for (int i = 0; i < NREGW; ++i) {
+      const char* src = blk[BPS == 1 ? 0 : rblk[i]] + roff[i] + loff[i];
+      char* dst = &s_kv[0][0] + boff + rdst[i];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+  };
+
+  // Table entries inside the loop come from LDS: windows of 64 entries are
+  // copied in by wavefront 0 into a ring of two, three stages before their
+  // first use (the copy stays clear of every wait until the next stage's,
+  // and a barrier publishes it).  Lane l copies the entry of block 64 w + l,
+  // clamped into the context (entries past it are never used).  A scalar
+  // load in flight would make every LDS wait of a stage wait for it too.
+  constexpr int SPW = 64 / BPS;                       // stages per window
+  auto window_copy = [&](int w) {
+    const int lb = max(min(64 * w + lane, ctx_blocks - 1), 0);
+    const int32_t* src = table_v + lb;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)s_ent[w & 1], 4,
+                                     0, 0);
+  };
+  // the entries of stage t (BPS <= 2), read from its window as one vector
+  typedef __attribute__((ext_vector_type(2))) int int2_t;
+  auto entries_read = [&](int t) -> int2_t {
+    const int32_t* w = s_ent[(t / SPW) & 1] + (t % SPW) * BPS;
+    if constexpr (BPS == 2) return *reinterpret_cast<const int2_t*>(w);
+    else return int2_t{w[0], 0};
+  };
+  auto entries_s = [&](int t, int (&e)[BPS]) {
+#pragma unroll
+    for (int bi = 0; bi < BPS; ++bi) {
+      const int lb = t * BPS + bi;
+      e[bi] = lb < ctx_blocks ? table[lb] : 0;
+    }
+  };
+
+  // ---- the products ----
+  // Row limits are non-decreasing in the row, so the wavefront's valid rows
+  // attend at least keys 0 .. wmin-1 and at most 0 .. wmax-1: stages below
+  // wmin need no logit mask, stages from wmax on give every row weight 0.
+  const int wrow0 = row0 + wave * 16 * R;
+  const int wrow1 = min(wrow0 + 16 * R, rows) - 1;
+  auto lim_of = [&](int row) {
+    return CAUSAL ? max(min(K, K - nq + row / G + 1), 0) : K;
+  };
+  const int wmin = wrow0 <= wrow1 ? lim_of(wrow0) : 0;
+  const int wmax = wrow0 <= wrow1 ? lim_of(wrow1) : 0;
+
+  // Logits are taken as raw products times |scale|: a negative scale flips
+  // the sign of Q (exact), so the row maximum of the raw products scales to
+  // the maximum of the logits.
+  const float sl = fabsf(p.qk_scale_log2);
+
+  // running maximum starts finite, so that exp2(logit - m) needs no guard:
+  // a masked logit (-inf) gives 0 whatever m is
+  float m[R], l[R];
+  float4_t acc[R][NPV];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = -__FLT_MAX__;
+    l[r] = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < NPV; ++jj) acc[r][jj] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // K operand of sub-tile u, chunk cc: key 16u + n, dims 32 cc + 8 g .. +7
+  auto k_operand = [&](const char* kb, int u, int cc) -> u32x4_t {
+    const int kk = 16 * u + n;
+    const int byte = (32 * cc + 8 * g) * ESZ;
+    const char* src = kb + kk * ROWB + (((byte / 16) ^ (kk % GPR)) * 16) + byte % 16;
+    if constexpr (ESZ == 2) {
+      return *reinterpret_cast<const u32x4_t*>(src);
+    } else {
+      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src);
+      return u32x4_t{M::template fp8x2<false>(w[0]), M::template fp8x2<true>(w[0]),
+                     M::template fp8x2<false>(w[1]), M::template fp8x2<true>(w[1])};
+    }
+  };
+  // V operand of product jj: dim 16 jj + n, keys 4g..4g+3 (quad g) and
+  // 16+4g..16+4g+3 (quad 4+g) of the stage
+  auto quad_at = [&](const char* vb, int q) {
+    return vb + (q / QPR) * VREG + (q % QPR) * QB;
+  };
+  auto v_operand = [&](const char* vb, int jj) -> u32x4_t {
+    const char* a = quad_at(vb, g) + (16 * jj + n) * 4 * ESZ;
+    const char* b2 = quad_at(vb, 4 + g) + (16 * jj + n) * 4 * ESZ;
+    if constexpr (ESZ == 2) {
+      // volatile: keeps each half a read of its own, straight into its
+      // registers (paired reads of neighbouring products need moves)
+      const u32x2_t x = *(const volatile LdsU32x2*)a;
+      const u32x2_t y = *(const volatile LdsU32x2*)b2;
+      return u32x4_t{x[0], x[1], y[0], y[1]};
+    } else {
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(a);
+      const uint32_t y = *reinterpret_cast<const uint32_t*>(b2);
+      return u32x4_t{MV::template fp8x2<false>(x), MV::template fp8x2<true>(x),
+                     MV::template fp8x2<false>(y), MV::template fp8x2<true>(y)};
+    }
+  };
+
+  // One stage.  MASK: some row of the wavefront stops inside the stage (its
+  // logits are masked by the row limit, and V elements of tokens past the
+  // context are zeroed); otherwise every key of the stage counts for every
+  // valid row and the logits go straight from the products to exp2.
+  auto compute = [&](auto mask_tag, int t, int boff) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* kb = &s_kv[0][0] + boff;
+    const char* vb = kb + KB;
+    const int key0 = t * kPfKeys;
+    // raw products of keys key0 + 16u + 4g + i, per row block
+    float4_t sc[R][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) sc[r][u] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < NQK; ++cc) {
+        const u32x4_t ka = k_operand(kb, u, cc);
+#pragma unroll
+        for (int r = 0; r < R; ++r) sc[r][u] = M::qk(ka, qb[r][cc], sc[r][u]);
       }
-      float pr[4];
+    }
+    // Row maxima of the stage's logits, and the weights exp2(logit - m) taken
+    // at once with the running maximum m (they are recomputed in the rare
+    // stage that moves m, below), so the exponentials of one product chain
+    // overlap the matrix products of the others.
+    float x[R][8], mt[R], pr[R][8];
+    bool grow = false;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = ok[r] ? exp2_hw(x[r] - m) : 0.0f;
-      const uint32_t p01 = MV::pack(pr[0], pr[1]);
-      const uint32_t p23 = MV::pack(pr[2], pr[3]);
-      u32x2_t pl = {0u, 0u};
-      if constexpr (kSplitP) {
-        pl = u32x2_t{MV::pack(pr[0] - MV::lo(p01), pr[1] - MV::hi(p01)),
-                     MV::pack(pr[2] - MV::lo(p23), pr[3] - MV::hi(p23))};
-        l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    for (int r = 0; r < R; ++r) {
+      if constexpr (MASK) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int key = key0 + 16 * (i >> 2) + 4 * g + (i & 3);
+          x[r][i] = key < lim[r] ? sc[r][i >> 2][i & 3] * sl : kNegInfP;
+        }
+        mt[r] = max8(x[r]);
       } else {
-        l += (MV::lo(p01) + MV::hi(p01)) + (MV::lo(p23) + MV::hi(p23));
-      }
-      const u32x2_t pb = {p01, p23};
-      uint32_t keep0 = 0xFFFFFFFFu, keep1 = 0xFFFFFFFFu;
-      if (vmask) {
-        const int t0 = 16 * u + 4 * g;
-        keep0 = (t0 + 0 < last_len ? 0x0000FFFFu : 0u) | (t0 + 1 < last_len ? 0xFFFF0000u : 0u);
-        keep1 = (t0 + 2 < last_len ? 0x0000FFFFu : 0u) | (t0 + 3 < last_len ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[r][i] = sc[r][i >> 2][i & 3];
+        mt[r] = max8(x[r]) * sl;
       }
 #pragma unroll
-      for (int j = 0; j < NPV; ++j) {
-        u32x2_t a = v_operand(vd[u][j / E], j % E);
-        if (vmask) a = u32x2_t{a[0] & keep0, a[1] & keep1};
-        acc[j] = MV::pv(a, pb, acc[j]);
-      }
-      if constexpr (kSplitP) {
+      for (int i = 0; i < 8; ++i)
+        pr[r][i] = exp2_hw(MASK ? x[r][i] - m[r] : __builtin_fmaf(x[r][i], sl, -m[r]));
+      grow |= mt[r] > m[r] + kSlackP;
+    }
+    // (keeps the weights computed here, ahead of the branch: left alone, the
+    // compiler would move them into the arm that uses them)
 #pragma unroll
-        for (int j = 0; j < NPV; ++j) {
-          u32x2_t a = v_operand(vd[u][j / E], j % E);
-          if (vmask) a = u32x2_t{a[0] & keep0, a[1] & keep1};
-          acc[j] = MV::pv(a, pl, acc[j]);
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(pr[r][i]));
+    // the weights packed as the PV B operand, their sum, then the PV products
+    auto weights_pv = [&]() {
+      u32x4_t pb[R], pl[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = MV::pack_pk(pr[r][2 * k], pr[r][2 * k + 1]);
+        pb[r] = u32x4_t{w[0], w[1], w[2], w[3]};
+        if constexpr (kSplitP) {
+          uint32_t v2[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            v2[k] = MV::pack_pk(pr[r][2 * k] - MV::lo(w[k]), pr[r][2 * k + 1] - MV::hi(w[k]));
+          pl[r] = u32x4_t{v2[0], v2[1], v2[2], v2[3]};
+          float sum = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sum += pr[r][i];
+          l[r] += sum;
+        } else {
+          // the sum of the weights as they enter the product
+          float lr = l[r];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) lr = MV::sum2(w[k], lr);
+          l[r] = lr;
         }
       }
+      // V elements of tokens past the context (a NaN there must not reach
+      // the product, even with weight 0)
+      uint32_t keep[4];
+      if constexpr (MASK) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int t0 = key0 + 16 * (k >> 1) + 4 * g + 2 * (k & 1);
+          keep[k] = (t0 < K ? 0x0000FFFFu : 0u) | (t0 + 1 < K ? 0xFFFF0000u : 0u);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < NPV; ++jj) {
+        u32x4_t va = v_operand(vb, jj);
+        if constexpr (MASK)
+          va = u32x4_t{va[0] & keep[0], va[1] & keep[1], va[2] & keep[2], va[3] & keep[3]};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          acc[r][jj] = MV::qk(va, pb[r], acc[r][jj]);
+          if constexpr (kSplitP) acc[r][jj] = MV::qk(va, pl[r], acc[r][jj]);
+        }
+      }
+    };
+    // Lazy rescale: the running maximum moves only when some row's stage
+    // maximum passes it by more than the slack (weights stay below 2^slack);
+    // then the accumulators are rescaled and the stage's weights recomputed.
+    // Both arms end in the products, so the accumulators are rewritten in
+    // place on either path.
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float mm = mt[r];
+        mm = __builtin_elementwise_maximum(mm, __shfl_xor(mm, 16, 64));
+        mm = __builtin_elementwise_maximum(mm, __shfl_xor(mm, 32, 64));
+        const float mn = fmaxf(m[r], mm);
+        const float alpha = exp2_hw(m[r] - mn);
+        m[r] = mn;
+        l[r] *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < NPV; ++jj) acc[r][jj] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pr[r][i] = exp2_hw(MASK ? x[r][i] - m[r] : __builtin_fmaf(x[r][i], sl, -m[r]));
+      }
+      weights_pv();
+    } else {
+      weights_pv();
     }
   };
 
+  // Q is loaded behind the first stage's copies and waited for together with
+  // them, before the loop: a load still pending at the loop entry would make
+  // every stage wait for all of its copies in flight.
+  int ecur[BPS];                                      // entries of stage t + 2
+  if (nstages > 0) {
+    int e0[BPS];
+    entries_s(0, e0);
+    stage_copy(0, 0, e0);
+    if (wave == 0 && nstages > 3) window_copy(0);
+  }
 #pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u) issue(kb[u], vb[u], u);
-  for (int t0 = 0; t0 < ntiles; t0 += NBUF) {
+  for (int r = 0; r < R; ++r) {
+    const char* qrow = reinterpret_cast<const char*>(p.q) +
+                       ((int64_t)(q0 + qi[r]) * p.q_token_stride + (int64_t)hh[r] * D) * 2;
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      const int t = t0 + u;
-      issue(kb[(u + NBUF - 1) % NBUF], vb[(u + NBUF - 1) % NBUF], t + NBUF - 1);
-      if (t < ntiles) process(kb[u], vb[u], t);
-    }
+    for (int cc = 0; cc < NQK; ++cc)
+      qb[r][cc] = ok_row[r] ? *reinterpret_cast<const u32x4_t*>(qrow + (32 * cc + 8 * g) * 2)
+                            : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  entries_s(2, ecur);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  if (p.qk_scale_log2 < 0.0f) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int cc = 0; cc < NQK; ++cc) qb[r][cc] ^= 0x80008000u;
+  }
+  if (nstages > 1) {
+    int e1[BPS];
+    entries_s(1, e1);
+    stage_copy(1, STAGE, e1);
   }
 
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  // Stage t is copied two stages ahead.  Waits are explicit (the barrier
+  // here is the bare instruction, whose implied fence would wait for every
+  // copy in flight): each lane waits for its own copies of stage t (those of
+  // stage t+1 may stay in flight) and for its LDS reads of stage t-1, then the
+  // barrier makes stage t complete for all and frees stage t-1's buffer, which
+  // receives stage t+2.  Every wavefront copies and meets every barrier; it
+  // computes only the stages some row of it attends.  The buffers rotate:
+  // stage t in buffer t % 3.
+  int cb = 0, nb = 2 * STAGE;                         // byte offsets: compute, copy
+  int2_t ev = int2_t{0, 0};
+  for (int t = 0; t < nstages; ++t) {
+    if (t + 1 < nstages) __builtin_amdgcn_s_waitcnt(kWaitVm0 | NREGW);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (t > 0) {                                      // entries read in the last stage
+      ecur[0] = __builtin_amdgcn_readfirstlane(ev[0]);
+      if constexpr (BPS == 2) ecur[1] = __builtin_amdgcn_readfirstlane(ev[1]);
+    }
+    if (t + 2 < nstages) {
+      // the window of stage t+4 when it opens one: its copy precedes this
+      // stage's copies, so the next stage's wait covers it
+      if (wave == 0 && t + 4 < nstages && (t + 4) % SPW == 0) window_copy((t + 4) / SPW);
+      stage_copy(t + 2, nb, ecur);
+    }
+    const int key0 = t * kPfKeys;
+    if (key0 < wmax) {
+      if (key0 + kPfKeys > wmin) compute(std::true_type{}, t, cb);
+      else compute(std::false_type{}, t, cb);
+    }
+    // entries of stage t+3, for the next stage's copy (its window arrived
+    // with this stage's barrier)
+    if (t + 3 < nstages) ev = entries_read(t + 3);
+    cb = cb == 2 * STAGE ? 0 : cb + STAGE;
+    nb = nb == 2 * STAGE ? 0 : nb + STAGE;
+  }
+
   // a row with no key gives zeros; a bad table entry NaN
-  const float inv = tw.bad ? __builtin_nanf("") : (l > 0.0f ? p.v_scale / l : 0.0f);
-  float4_t o[NPV];
+  float4_t o[R][NPV];
 #pragma unroll
-  for (int j = 0; j < NPV; ++j)
+  for (int r = 0; r < R; ++r) {
+    float lt = l[r];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const float inv = bad_entry ? __builtin_nanf("") : (lt > 0.0f ? p.v_scale / lt : 0.0f);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[j][r] = acc[j][r] * inv;
-  write_out(o);
+    for (int jj = 0; jj < NPV; ++jj) o[r][jj] = acc[r][jj] * inv;
+  }
+  store_rows(o);
 }
+
+constexpr int kPfRowBlocks = 2;       // row blocks of 16 per wavefront
 
 template <typename QT, typename CT, int D, int BS>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
+  constexpr int ROWS = PfShape<QT, CT, D, BS, kPfRowBlocks>::ROWS;
   const int G = p.num_heads / p.num_kv_heads;
   const int64_t rows = (int64_t)p.max_seqlen_q * G;
-  const unsigned bx = (unsigned)((rows + kRowsPerWg - 1) / kRowsPerWg);
-  const dim3 grid(bx, p.num_seqs, p.num_kv_heads);
+  const int chunks = (int)((rows + ROWS - 1) / ROWS);
+  const int64_t items = (int64_t)p.num_seqs * p.num_kv_heads;
+  const int64_t groups = (items + kXcds - 1) / kXcds;
+  const int64_t blocks = groups * chunks * kXcds;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
   if (p.causal)
-    hipLaunchKernelGGL((prefill_mfma_kernel<QT, CT, D, BS, true>), grid, dim3(64 * kPrefillWaves),
-                       0, stream, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<QT, CT, D, BS, true, kPfRowBlocks>),
+                       dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, p, chunks);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<QT, CT, D, BS, false>), grid,
-                       dim3(64 * kPrefillWaves), 0, stream, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<QT, CT, D, BS, false, kPfRowBlocks>),
+                       dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, p, chunks);
   return hipGetLastError();
 }
 
