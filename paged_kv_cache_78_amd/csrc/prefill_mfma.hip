@@ -354,12 +354,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
   };
 
-  // One stage.  MASK: some row of the wavefront stops inside the stage (its
-  // logits are masked by the row limit, and V elements of tokens past the
-  // context are zeroed); otherwise every key of the stage counts for every
-  // valid row and the logits go straight from the products to exp2.
-  auto compute = [&](auto mask_tag, int t, int boff) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // One stage.  The weights come from one of two paths (masked: some row of
+  // the wavefront stops inside the stage, its logits past the row limit are
+  // -inf; unmasked: every key counts for every valid row and the logits go
+  // straight from the products to exp2), then the accumulators meet a single
+  // product path, so each product updates them in place.
+  auto compute = [&](bool masked, int t, int boff) {
     const char* kb = &s_kv[0][0] + boff;
     const char* vb = kb + KB;
     const int key0 = t * kPfKeys;
@@ -376,91 +376,45 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         for (int r = 0; r < R; ++r) sc[r][u] = M::qk(ka, qb[r][cc], sc[r][u]);
       }
     }
-    // Row maxima of the stage's logits, and the weights exp2(logit - m) taken
-    // at once with the running maximum m (they are recomputed in the rare
-    // stage that moves m, below), so the exponentials of one product chain
-    // overlap the matrix products of the others.
-    float x[R][8], mt[R], pr[R][8];
-    bool grow = false;
+    // the V operands, read while the weights are computed
+    u32x4_t va[NPV];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if constexpr (MASK) {
+    for (int jj = 0; jj < NPV; ++jj) va[jj] = v_operand(vb, jj);
+    // Row maxima of the stage's logits, and the weights exp2(logit - m) taken
+    // at once with the running maximum m (recomputed in the rare stage that
+    // moves m, below), so the exponentials of one product chain overlap the
+    // matrix products of the others.
+    float mt[R], pr[R][8];
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int key = key0 + 16 * (i >> 2) + 4 * g + (i & 3);
-          x[r][i] = key < lim[r] ? sc[r][i >> 2][i & 3] * sl : kNegInfP;
+          x[i] = key < lim[r] ? sc[r][i >> 2][i & 3] * sl : kNegInfP;
         }
-        mt[r] = max8(x[r]);
-      } else {
+        mt[r] = max8(x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[r][i] = sc[r][i >> 2][i & 3];
-        mt[r] = max8(x[r]) * sl;
+        for (int i = 0; i < 8; ++i) pr[r][i] = exp2_hw(x[i] - m[r]);
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        pr[r][i] = exp2_hw(MASK ? x[r][i] - m[r] : __builtin_fmaf(x[r][i], sl, -m[r]));
-      grow |= mt[r] > m[r] + kSlackP;
-    }
-    // (keeps the weights computed here, ahead of the branch: left alone, the
-    // compiler would move them into the arm that uses them)
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(pr[r][i]));
-    // the weights packed as the PV B operand, their sum, then the PV products
-    auto weights_pv = [&]() {
-      u32x4_t pb[R], pl[R];
+    } else {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        uint32_t w[4];
+        float x[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w[k] = MV::pack_pk(pr[r][2 * k], pr[r][2 * k + 1]);
-        pb[r] = u32x4_t{w[0], w[1], w[2], w[3]};
-        if constexpr (kSplitP) {
-          uint32_t v2[4];
+        for (int i = 0; i < 8; ++i) x[i] = sc[r][i >> 2][i & 3];
+        mt[r] = max8(x) * sl;
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            v2[k] = MV::pack_pk(pr[r][2 * k] - MV::lo(w[k]), pr[r][2 * k + 1] - MV::hi(w[k]));
-          pl[r] = u32x4_t{v2[0], v2[1], v2[2], v2[3]};
-          float sum = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sum += pr[r][i];
-          l[r] += sum;
-        } else {
-          // the sum of the weights as they enter the product
-          float lr = l[r];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) lr = MV::sum2(w[k], lr);
-          l[r] = lr;
-        }
+        for (int i = 0; i < 8; ++i) pr[r][i] = exp2_hw(__builtin_fmaf(x[i], sl, -m[r]));
       }
-      // V elements of tokens past the context (a NaN there must not reach
-      // the product, even with weight 0)
-      uint32_t keep[4];
-      if constexpr (MASK) {
+    }
+    bool grow = false;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int t0 = key0 + 16 * (k >> 1) + 4 * g + 2 * (k & 1);
-          keep[k] = (t0 < K ? 0x0000FFFFu : 0u) | (t0 + 1 < K ? 0xFFFF0000u : 0u);
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < NPV; ++jj) {
-        u32x4_t va = v_operand(vb, jj);
-        if constexpr (MASK)
-          va = u32x4_t{va[0] & keep[0], va[1] & keep[1], va[2] & keep[2], va[3] & keep[3]};
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          acc[r][jj] = MV::qk(va, pb[r], acc[r][jj]);
-          if constexpr (kSplitP) acc[r][jj] = MV::qk(va, pl[r], acc[r][jj]);
-        }
-      }
-    };
+    for (int r = 0; r < R; ++r) grow |= mt[r] > m[r] + kSlackP;
     // Lazy rescale: the running maximum moves only when some row's stage
     // maximum passes it by more than the slack (weights stay below 2^slack);
     // then the accumulators are rescaled and the stage's weights recomputed.
-    // Both arms end in the products, so the accumulators are rewritten in
-    // place on either path.
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -474,12 +428,76 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
         for (int jj = 0; jj < NPV; ++jj) acc[r][jj] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          pr[r][i] = exp2_hw(MASK ? x[r][i] - m[r] : __builtin_fmaf(x[r][i], sl, -m[r]));
+        for (int i = 0; i < 8; ++i) {
+          const int key = key0 + 16 * (i >> 2) + 4 * g + (i & 3);
+          pr[r][i] = key < lim[r] ? exp2_hw(__builtin_fmaf(sc[r][i >> 2][i & 3], sl, -m[r])) : 0.0f;
+        }
       }
-      weights_pv();
-    } else {
-      weights_pv();
+    }
+    // the weights packed as the PV B operand, their sum, then the products
+    u32x4_t pb[R], pl[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = MV::pack_pk(pr[r][2 * k], pr[r][2 * k + 1]);
+      pb[r] = u32x4_t{w[0], w[1], w[2], w[3]};
+      if constexpr (kSplitP) {
+        uint32_t v2[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          v2[k] = MV::pack_pk(pr[r][2 * k] - MV::lo(w[k]), pr[r][2 * k + 1] - MV::hi(w[k]));
+        pl[r] = u32x4_t{v2[0], v2[1], v2[2], v2[3]};
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sum += pr[r][i];
+        l[r] += sum;
+      } else {
+        // the sum of the weights as they enter the product
+        float lr = l[r];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lr = MV::sum2(w[k], lr);
+        l[r] = lr;
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < NPV; ++jj) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        acc[r][jj] = MV::qk(va[jj], pb[r], acc[r][jj]);
+        if constexpr (kSplitP) acc[r][jj] = MV::qk(va[jj], pl[r], acc[r][jj]);
+      }
+    }
+  };
+
+  // V elements of tokens past the context, in the last stage when the
+  // context ends inside it: zeroed in LDS by the wavefronts that copied V,
+  // once their copies have landed and before the barrier (a NaN there must
+  // not reach the product, even with weight 0).  Lane pairs (dim, quad) of
+  // the wavefront's regions.
+  auto zero_v_tail = [&](int t, int boff) {
+    const int j0 = K - t * kPfKeys;                   // first local token past the context
+    constexpr int QW = NREGW * QPR;                   // token quads of the wavefront
+    const int vr0 = (wave - 2) * NREGW;               // its first V region
+    for (int idx = lane; idx < QW * D; idx += 64) {
+      const int ql = idx / D, d = idx % D;
+      const int vr = vr0 + ql / QPR;
+      const int q = vr * QPR + ql % QPR;              // quad within the stage
+      if (4 * q + 3 < j0) continue;
+      char* at = &s_kv[0][0] + boff + KB + vr * VREG + (ql % QPR) * QB + d * 4 * ESZ;
+      if constexpr (ESZ == 2) {
+        u32x2_t v = *reinterpret_cast<u32x2_t*>(at);
+        const int e0 = j0 - 4 * q;                    // first element to clear (may be <= 0)
+        v[0] &= (e0 > 0 ? 0x0000FFFFu : 0u) | (e0 > 1 ? 0xFFFF0000u : 0u);
+        v[1] &= (e0 > 2 ? 0x0000FFFFu : 0u) | (e0 > 3 ? 0xFFFF0000u : 0u);
+        *reinterpret_cast<u32x2_t*>(at) = v;
+      } else {
+        uint32_t v = *reinterpret_cast<uint32_t*>(at);
+        const int e0 = j0 - 4 * q;
+        v &= (e0 > 0 ? 0x000000FFu : 0u) | (e0 > 1 ? 0x0000FF00u : 0u) |
+             (e0 > 2 ? 0x00FF0000u : 0u) | (e0 > 3 ? 0xFF000000u : 0u);
+        *reinterpret_cast<uint32_t*>(at) = v;
+      }
     }
   };
 
@@ -526,9 +544,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // stage t in buffer t % 3.
   int cb = 0, nb = 2 * STAGE;                         // byte offsets: compute, copy
   int2_t ev = int2_t{0, 0};
-  for (int t = 0; t < nstages; ++t) {
-    if (t + 1 < nstages) __builtin_amdgcn_s_waitcnt(kWaitVm0 | NREGW);
-    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  auto stage_begin = [&](int t) {
+    if (t + 1 < nstages) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0 | NREGW);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      if (!copies_k && t * kPfKeys + kPfKeys > K) zero_v_tail(t, cb);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
@@ -543,16 +565,27 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
       if (wave == 0 && t + 4 < nstages && (t + 4) % SPW == 0) window_copy((t + 4) / SPW);
       stage_copy(t + 2, nb, ecur);
     }
-    const int key0 = t * kPfKeys;
-    if (key0 < wmax) {
-      if (key0 + kPfKeys > wmin) compute(std::true_type{}, t, cb);
-      else compute(std::false_type{}, t, cb);
-    }
+  };
+  auto stage_end = [&](int t) {
     // entries of stage t+3, for the next stage's copy (its window arrived
     // with this stage's barrier)
     if (t + 3 < nstages) ev = entries_read(t + 3);
     cb = cb == 2 * STAGE ? 0 : cb + STAGE;
     nb = nb == 2 * STAGE ? 0 : nb + STAGE;
+  };
+  // The stages this wavefront computes come first, then those it only
+  // copies (two loops, so that no path of the first leaves the accumulators
+  // as they were, which would cost a copy of them per stage).
+  const int wstages = min(nstages, (wmax + kPfKeys - 1) / kPfKeys);
+  int t = 0;
+  for (; t < wstages; ++t) {
+    stage_begin(t);
+    compute(t * kPfKeys + kPfKeys > wmin, t, cb);
+    stage_end(t);
+  }
+  for (; t < nstages; ++t) {
+    stage_begin(t);
+    stage_end(t);
   }
 
   // a row with no key gives zeros; a bad table entry NaN
