@@ -122,26 +122,76 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int G = H / KVH;
   const int MB = p.max_blocks_per_seq;
 
-  // workgroup b runs on XCD b % 8: the chunks of item it = j / chunks * 8 +
-  // b % 8 (j = b / 8) all run on that XCD, the chunk with the most keys first
+  // Workgroup b runs on XCD b % 8, and each XCD starts its workgroups in
+  // the order of b / 8 as slots free up.  The chunks of an item (sequence,
+  // kv head) all run on the XCD item % 8, one after the other, the chunk
+  // with the most keys first (they share the item's K/V in that XCD's L2).
+  // Up to 64 sequences, each XCD's queue takes the sequences' items in the
+  // order of decreasing context (longest work first, so that the queue ends
+  // with short work); beyond that, in item order.
   const int b = blockIdx.x;
-  const int j = b / kXcds;
-  const int item = (j / chunks) * kXcds + b % kXcds;
-  if (item >= p.num_seqs * KVH) return;
-  const int c = chunks - 1 - j % chunks;
-  const int s = item / KVH;
-  const int kvh = item % KVH;
+  const int x = b % kXcds, jq = b / kXcds;
+  int s, c, kvh;
+  bool live;
+  if (p.num_seqs <= 64) {
+    // lane l: sequence l, its context (ties: the lower index first) and
+    // its items on this XCD
+    const int sl = lane < p.num_seqs ? lane : 0;
+    const int kl = p.context_lens[sl];
+    const int rr = ((x - sl * KVH) % kXcds + kXcds) % kXcds;   // its first kv head here
+    const int mult = lane < p.num_seqs && rr < KVH ? (KVH - 1 - rr) / kXcds + 1 : 0;
+    const int64_t key = ((int64_t)kl << 6) | (63 - lane);
+    // queue position of sequence l's first workgroup
+    int pos = 0;
+    for (int l2 = 0; l2 < p.num_seqs; ++l2) {
+      const int klo = __builtin_amdgcn_readlane(kl, l2);
+      const int m2 = __builtin_amdgcn_readlane(mult, l2);
+      const int64_t k2 = ((int64_t)klo << 6) | (63 - l2);
+      pos += k2 > key ? m2 * chunks : 0;
+    }
+    const uint64_t hit =
+        __builtin_amdgcn_ballot_w64(mult > 0 && pos <= jq && jq < pos + mult * chunks);
+    live = hit != 0;
+    const int gl = live ? (int)__builtin_ctzll(hit) : 0;
+    const int local = jq - __builtin_amdgcn_readlane(pos, gl);
+    s = gl;
+    c = chunks - 1 - local % chunks;
+    kvh = ((x - s * KVH) % kXcds + kXcds) % kXcds + kXcds * (local / chunks);
+  } else {
+    const int item = (jq / chunks) * kXcds + x;
+    live = item < p.num_seqs * KVH;
+    c = chunks - 1 - jq % chunks;
+    s = live ? item / KVH : 0;
+    kvh = item % KVH;
+  }
 
+  // The sequence's lengths and the table entries of its first three stages
+  // are loaded at once (indices clamped into the row; entries past the
+  // context are never used), and waited for together before any branch.
+  constexpr int NPRE = 3 * BPS;
+  int epre[NPRE];
   const int32_t q0 = p.cu_seqlens_q[s];
   const int32_t q1 = p.cu_seqlens_q[s + 1];
+  const int K = p.context_lens[s];
+  {
+    ConstTable* trow = (ConstTable*)(p.block_table + (int64_t)s * MB);
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) epre[i] = trow[min(i, MB - 1)];
+  }
+  const int total_q = p.total_q, max_seqlen_q = p.max_seqlen_q;
+  const int64_t q_token_stride = p.q_token_stride, num_blocks = p.num_blocks;
+  asm volatile("" ::"s"(q0), "s"(q1), "s"(K), "s"(total_q), "s"(max_seqlen_q));
+  asm volatile("" ::"s"(q_token_stride), "s"(num_blocks));
+#pragma unroll
+  for (int i = 0; i < NPRE; ++i) asm volatile("" ::"s"(epre[i]));
+  if (!live) return;
   const int nq = q1 - q0;
   // packed rows outside [0, total_q) are never touched
-  if (q0 < 0 || q1 > p.total_q || nq <= 0) return;
+  if (q0 < 0 || q1 > total_q || nq <= 0) return;
   const int rows = nq * G;
   const int row0 = c * ROWS;
   if (row0 >= rows) return;
-  const int K = p.context_lens[s];
-  const bool bad_len = K < 0 || K > MB * BS || nq > p.max_seqlen_q;
+  const bool bad_len = K < 0 || K > MB * BS || nq > max_seqlen_q;
 
   // this lane's rows (one per row block) and the keys each attends: 0 .. lim-1
   int qi[R], hh[R], lim[R];
@@ -203,13 +253,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // granules of key kk XOR-permuted by kk % GPR (so the 16 keys a K operand
   // read touches land in different banks); V region r holds token quads
   // r*QPR .. in the tile layout.
-  ConstTable* table = (ConstTable*)(p.block_table + (int64_t)s * MB);
   const int32_t* table_v = p.block_table + (int64_t)s * MB;
   const bool copies_k = wave < 2;
   const char* cache = reinterpret_cast<const char*>(copies_k ? p.k_cache : p.v_cache) +
                       (int64_t)kvh * TILE_BYTES;
   const int64_t block_stride = (int64_t)KVH * TILE_BYTES;
-  const uint32_t nb32 = (uint32_t)min(p.num_blocks, (int64_t)INT32_MAX);
+  const uint32_t nb32 = (uint32_t)min(num_blocks, (int64_t)INT32_MAX);
   bool bad_entry = false;
 
   // Every region lies in one cache block (KPR keys of K, QPR token quads of V,
@@ -282,12 +331,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     if constexpr (BPS == 2) return *reinterpret_cast<const int2_t*>(w);
     else return int2_t{w[0], 0};
   };
-  auto entries_s = [&](int t, int (&e)[BPS]) {
+  // entries of stage t < 3, from those loaded up front
+  auto entries_pre = [&](int t, int (&e)[BPS]) {
 #pragma unroll
-    for (int bi = 0; bi < BPS; ++bi) {
-      const int lb = t * BPS + bi;
-      e[bi] = lb < ctx_blocks ? table[lb] : 0;
-    }
+    for (int bi = 0; bi < BPS; ++bi) e[bi] = epre[t * BPS + bi];
   };
 
   // ---- the products ----
@@ -501,26 +548,27 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
   };
 
-  // Q is loaded behind the first stage's copies and waited for together with
-  // them, before the loop: a load still pending at the loop entry would make
-  // every stage wait for all of its copies in flight.
+  // Stage 0's copies, then Q, waited for together before stage 1's copies
+  // and the loop (a load the compiler still counts as pending at the loop
+  // entry would make every stage wait for all of its copies in flight; it
+  // does not count the copies when it checks an explicit wait against Q).
   int ecur[BPS];                                      // entries of stage t + 2
+  entries_pre(2, ecur);
   if (nstages > 0) {
     int e0[BPS];
-    entries_s(0, e0);
+    entries_pre(0, e0);
     stage_copy(0, 0, e0);
     if (wave == 0 && nstages > 3) window_copy(0);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       ((int64_t)(q0 + qi[r]) * p.q_token_stride + (int64_t)hh[r] * D) * 2;
+                       ((int64_t)(q0 + qi[r]) * q_token_stride + (int64_t)hh[r] * D) * 2;
 #pragma unroll
     for (int cc = 0; cc < NQK; ++cc)
       qb[r][cc] = ok_row[r] ? *reinterpret_cast<const u32x4_t*>(qrow + (32 * cc + 8 * g) * 2)
                             : u32x4_t{0u, 0u, 0u, 0u};
   }
-  entries_s(2, ecur);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   if (p.qk_scale_log2 < 0.0f) {
 #pragma unroll
@@ -530,7 +578,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   }
   if (nstages > 1) {
     int e1[BPS];
-    entries_s(1, e1);
+    entries_pre(1, e1);
     stage_copy(1, STAGE, e1);
   }
 

@@ -75,6 +75,16 @@ def test_chunks_against_oracle(dtype, H, KVH, D, BS):
     _check(b, f"{dtype} H{H} KVH{KVH} D{D} BS{BS}")
 
 
+def test_many_sequences():
+    """More than 64 sequences (the workgroup queue then runs item by item
+    instead of by decreasing context), with equal contexts among them."""
+    rng = np.random.default_rng(37)
+    q_lens = rng.integers(1, 24, size=70).tolist()
+    ctx = (rng.integers(0, 6, size=70) * 16).tolist()
+    b = workloads.poison_prefill(workloads.prefill_batch(37, q_lens, ctx, 4, 2, 64, 16, "f16"))
+    _check(b, "70 sequences")
+
+
 @pytest.mark.parametrize("H,KVH,D,BS", [(16, 2, 128, 16), (4, 4, 64, 32)])
 def test_fp8_cache(H, KVH, D, BS):
     b = workloads.prefill_batch(32, [9, 33, 1], [40, 0, 77], H, KVH, D, BS, "bf16", "e4m3fn")
