@@ -415,7 +415,9 @@ def bench_prefill(args, torch, pa, dev):
                    "total_query_tokens": T, "step": "pa_cache_write + pa_prefill"},
         "roofline": {"bound": "mfma", "kernel": "pa_prefill", "achieved": achieved,
                      "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_MFMA_F16_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_MFMA_F16_TFLOPS,
+                     "traffic": recorded_traffic("pa_prefill", "llama7b_prefill_chunks",
+                                                 kernel_source_hash()),
                      "algorithmic_flops_per_launch": flops, "kernel_ms": kern_ms,
                      "kernel_sources": kernel_source_hash()},
         "cpu_baseline": cpu,

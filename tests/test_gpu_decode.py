@@ -211,6 +211,50 @@ def test_single_partition_equals_one_pass_bit_for_bit():
 # ----------------------------------------------------------------------------
 # cache write
 
+def _run_slots(BS):
+    """Slot runs of a prefill-like write: an unaligned run across a block
+    boundary, an aligned whole quad, a quad with a skipped (-1) token, a quad
+    in reversed token order and a lone token."""
+    runs = [list(range(5, 5 + 2 * BS + 3)),              # unaligned, crosses blocks
+            list(range(4 * BS, 4 * BS + 4)),              # one whole quad
+            [5 * BS + 8, 5 * BS + 9, -1, 5 * BS + 11],    # a token skipped inside a quad
+            [6 * BS + 3, 6 * BS + 2, 6 * BS + 1, 6 * BS], # reversed order
+            [7 * BS + 6]]
+    return [x for r in runs for x in r]
+
+
+@pytest.mark.parametrize("cache_fmt,D,BS", [("f16", 128, 16), ("bf16", 64, 32),
+                                            ("e4m3fn", 128, 16), ("e4m3fn", 64, 32)])
+def test_cache_write_runs_bit_exact(cache_fmt, D, BS):
+    """Whole token quads are written four tokens at a time, the rest token by
+    token: both against the oracle's write, bit for bit."""
+    gen = torch.Generator().manual_seed(11)
+    KVH, NB = 3, 9
+    slots = torch.tensor(_run_slots(BS), dtype=torch.int32)
+    T = slots.numel()
+    in_dt = torch.bfloat16 if cache_fmt == "bf16" else torch.float16
+    k = torch.randn((T, KVH, D), generator=gen).to(in_dt)
+    v = torch.randn((T, KVH, D), generator=gen).to(in_dt)
+    if cache_fmt == "e4m3fn":
+        kc0 = torch.randint(0, 256, (NB, KVH, BS, D), generator=gen, dtype=torch.uint8)
+        vc0 = torch.randint(0, 256, (NB, KVH, BS // 4, D, 4), generator=gen, dtype=torch.uint8)
+        kc0[(kc0 & 0x7F) == 0x7F] = 0                    # no NaN codes in the pool
+        vc0[(vc0 & 0x7F) == 0x7F] = 0
+        kc, vc = kc0.view(torch.float8_e4m3fn), vc0.view(torch.float8_e4m3fn)
+        ks, vs = 0.5, 0.25
+    else:
+        kc = torch.randn((NB, KVH, BS, D), generator=gen).to(in_dt)
+        vc = torch.randn((NB, KVH, BS // 4, D, 4), generator=gen).to(in_dt)
+        ks = vs = 1.0
+    gk, gv = kc.to(DEV), vc.to(DEV)
+    pa.cache_write(k.to(DEV), v.to(DEV), gk, gv, slots.to(DEV), k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    ok, ov = oracle.cache_write(to_numpy_bits(k), to_numpy_bits(v), to_numpy_bits(kc),
+                                to_numpy_bits(vc), slots.numpy(), BS, cache_fmt, ks, vs)
+    assert to_numpy_bits(gk).tobytes() == ok.tobytes()
+    assert to_numpy_bits(gv).tobytes() == ov.tobytes()
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_cache_write_16bit_bit_exact(dtype):
     wl = workloads.llama7b_mha(seed=9, num_seqs=9, len_range=(0, 100), num_heads=4,
