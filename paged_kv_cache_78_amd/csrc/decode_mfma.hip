@@ -89,6 +89,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int H = p.num_heads;
   const int KVH = p.num_kv_heads;
   int kvh, s, part;
+  int len_ranked = -1;                // the sequence's length, when the ranking read it
   if constexpr (PART) {
     kvh = blockIdx.x;
     s = blockIdx.y;
@@ -100,12 +101,13 @@ void decode_mfma_kernel(const DecodeParams p) {
     const int rank = pos / KVH;
     kvh = pos % KVH;
     s = p.order_by_length
-            ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist + wave * kSchedKeys, lane)
+            ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist + wave * kSchedKeys, lane,
+                          len_ranked)
             : rank;
     part = 0;
   }
   const int G = H / KVH;
-  const int L = p.context_lens[s];
+  const int L = (!PART && p.order_by_length) ? len_ranked : p.context_lens[s];
   const int MB = p.max_blocks_per_seq;
 
   const int tiles_per_part = PART ? p.partition_size / BS : 0;

@@ -186,6 +186,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   float* s_p = s_p_all + wave * BS;
   const int H = p.num_heads;
   int h, s, part;
+  int len_ranked = -1;                // the sequence's length, when the ranking read it
   if constexpr (PART) {
     h = blockIdx.x;
     s = blockIdx.y;
@@ -199,11 +200,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
     const int rank = pos / H;
     h = pos % H;
     s = p.order_by_length
-            ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist + wave * kSchedKeys, lane)
+            ? seq_by_rank(p.context_lens, p.num_seqs, BS, rank, s_hist + wave * kSchedKeys, lane,
+                          len_ranked)
             : rank;
     part = 0;
   }
-  const int L = p.context_lens[s];
+  const int L = (!PART && p.order_by_length) ? len_ranked : p.context_lens[s];
   const int MB = p.max_blocks_per_seq;
 
   // token range of this workgroup and of this wavefront

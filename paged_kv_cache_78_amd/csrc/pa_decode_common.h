@@ -66,12 +66,33 @@ __device__ __forceinline__ int sched_key(int len, int block_size) {
   return (kSchedKeys - 1) - (nb < kSchedKeys - 1 ? nb : kSchedKeys - 1);
 }
 
+// Up to kCachedSeqs sequences, each lane keeps the lengths it loaded (one
+// load per sequence, all issued at once) for the second pass and for the
+// returned length; beyond that, they are loaded again.
+constexpr int kCachedSeqs = 4 * kWave;
+
 __device__ __forceinline__ int seq_by_rank(const int32_t* context_lens, int num_seqs,
-                                           int block_size, int rank, int* hist, int lane) {
+                                           int block_size, int rank, int* hist, int lane,
+                                           int& len) {
+  constexpr int NC = kCachedSeqs / kWave;
+  const bool cached = num_seqs <= kCachedSeqs;
+  int cl[NC];
+  if (cached) {
+    // indices clamped into the array, so every load is issued unconditionally
+#pragma unroll
+    for (int i = 0; i < NC; ++i) cl[i] = context_lens[min(lane + i * kWave, num_seqs - 1)];
+  }
 #pragma unroll
   for (int i = 0; i < kSchedKeys / kWave; ++i) hist[lane + i * kWave] = 0;
   __syncthreads();
-  for (int s = lane; s < num_seqs; s += kWave) atomicAdd(&hist[sched_key(context_lens[s], block_size)], 1);
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (lane + i * kWave < num_seqs) atomicAdd(&hist[sched_key(cl[i], block_size)], 1);
+  } else {
+    for (int s = lane; s < num_seqs; s += kWave)
+      atomicAdd(&hist[sched_key(context_lens[s], block_size)], 1);
+  }
   __syncthreads();
   // lane owns keys [4 lane, 4 lane + 4): exclusive prefix over lanes
   int c[4];
@@ -107,19 +128,40 @@ __device__ __forceinline__ int seq_by_rank(const int32_t* context_lens, int num_
   key = __builtin_amdgcn_readlane(key, owner);
   int target = rank - __builtin_amdgcn_readlane(start, owner);
   // the target-th sequence (in index order) carrying that key
-  for (int base = 0; base < num_seqs; base += kWave) {
-    const int s = base + lane;
-    const bool match = s < num_seqs && sched_key(context_lens[s], block_size) == key;
-    const uint64_t m = __builtin_amdgcn_ballot_w64(match);
-    const int cnt = __builtin_popcountll(m);
-    if (target < cnt) {
-      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(match && below == target);
-      return base + (int)__builtin_ctzll(hit);
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const bool match = lane + i * kWave < num_seqs && sched_key(cl[i], block_size) == key;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(match);
+      const int cnt = __builtin_popcountll(m);
+      if (target < cnt) {
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(match && below == target);
+        const int l = (int)__builtin_ctzll(hit);
+        len = __builtin_amdgcn_readlane(cl[i], l);
+        return i * kWave + l;
+      }
+      target -= cnt;
     }
-    target -= cnt;
+  } else {
+    for (int base = 0; base < num_seqs; base += kWave) {
+      const int s = base + lane;
+      const bool match = s < num_seqs && sched_key(context_lens[s], block_size) == key;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(match);
+      const int cnt = __builtin_popcountll(m);
+      if (target < cnt) {
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(match && below == target);
+        const int sq = base + (int)__builtin_ctzll(hit);
+        len = context_lens[sq];
+        return sq;
+      }
+      target -= cnt;
+    }
   }
+  len = context_lens[0];
   return 0;   // rank >= num_seqs: not reached for valid launches
 }
 
