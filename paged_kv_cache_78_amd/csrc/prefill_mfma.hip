@@ -26,18 +26,22 @@
 // 8 contraction elements of lane group g are the keys 4g..4g+3 of both
 // sub-tiles, which is where S^T put them: the weights go into the B operand
 // without any exchange, and the V operand reads the matching token quads.
-// LDS rows are padded (K by 16 bytes per key, V by 128 bytes per token quad)
-// so that the operand reads hit every bank once.
+// The 16-byte granules of each K row in LDS are XOR-permuted by the key and
+// V's token-quad regions are padded by 128 bytes, so that the operand reads
+// hit every bank once.  The copies go from global memory straight into LDS
+// (global_load_lds), three stages in a ring.
 //
 // Work mapping: workgroups go to the XCDs round robin, so the chunks of one
 // (sequence, kv head) are given workgroup indices that land on the same XCD
-// and share its L2; causal chunks with more keys go first.
+// and share its L2, one after the other, the chunk with more keys first;
+// the sequences' items are taken by decreasing context.
 //
 // Weight precision, fp8 decoding and masking follow the decode kernels: P in
 // f16 (f16 and fp8 caches) or split into two bf16 parts (bf16 caches); keys
 // past a row's limit get a -inf logit and weight 0, V elements of tokens past
 // the context are zeroed before the product (a NaN in an unused slot must not
-// reach it), and table entries past the context are never read.
+// reach it), and table entries past the context are never used (a few past
+// it, inside the row, may be read).
 #include <type_traits>
 
 #include "mfma_common.h"
@@ -111,6 +115,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 
   __shared__ __attribute__((aligned(16))) char s_kv[NST][STAGE];
   __shared__ __attribute__((aligned(16))) int32_t s_ent[2][64];   // table windows
+  __shared__ int32_t s_bad[kPfWaves];   // a wavefront met a bad table entry
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -168,7 +173,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // The sequence's lengths and the table entries of its first three stages
   // are loaded at once (indices clamped into the row; entries past the
   // context are never used), and waited for together before any branch.
-  constexpr int NPRE = 3 * BPS;
+  constexpr int NPRE = 3;
+  const int wblk = (16 * (wave & 1)) / BS;   // the stage block whose half this wavefront copies
   int epre[NPRE];
   const int32_t q0 = p.cu_seqlens_q[s];
   const int32_t q1 = p.cu_seqlens_q[s + 1];
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   {
     ConstTable* trow = (ConstTable*)(p.block_table + (int64_t)s * MB);
 #pragma unroll
-    for (int i = 0; i < NPRE; ++i) epre[i] = trow[min(i, MB - 1)];
+    for (int i = 0; i < NPRE; ++i) epre[i] = trow[min(i * BPS + wblk, MB - 1)];
   }
   const int total_q = p.total_q, max_seqlen_q = p.max_seqlen_q;
   const int64_t q_token_stride = p.q_token_stride, num_blocks = p.num_blocks;
@@ -261,52 +267,45 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const uint32_t nb32 = (uint32_t)min(num_blocks, (int64_t)INT32_MAX);
   bool bad_entry = false;
 
-  // Every region lies in one cache block (KPR keys of K, QPR token quads of V,
-  // both dividing the block, and a stage starts on a block boundary), so its
-  // source is block address + a fixed offset + a per-lane offset, all but
-  // the block address fixed for the loop.
+  // The regions of a wavefront are half a stage: the 16 keys 16 (wave % 2)
+  // .. of K, or the 4 token quads (16 tokens) of V starting there, always
+  // inside one cache block (block wblk of the stage, at byte offset roff0),
+  // consecutive 1 KiB apart in the source.  So a stage's copy needs one
+  // table entry per wavefront, and the sources are block address + per-lane
+  // offsets fixed for the loop.
+  const int half = wave & 1;
+  const int roff0 = copies_k ? ((16 * half) % BS) * ROWB : ((4 * half) % (BS / 4)) * QB;
+  const int rdst0 = copies_k ? wave * NREGW * 1024 : KB + half * NREGW * VREG;
+  const int rstep = copies_k ? 1024 : VREG;
   const int b16 = 16 * lane;
-  int rblk[NREGW], roff[NREGW], rdst[NREGW], loff[NREGW];
+  int loff[NREGW];                                    // region i: source byte offset
 #pragma unroll
   for (int i = 0; i < NREGW; ++i) {
-    const int ri = wave * NREGW + i;
     if (copies_k) {
-      const int k0 = ri * KPR;                          // first key of the region
-      const int kk = k0 + b16 / ROWB;
-      rblk[i] = k0 / BS;
-      roff[i] = (k0 % BS) * ROWB;
-      rdst[i] = ri * 1024;
-      loff[i] = (b16 / ROWB) * ROWB + (((b16 % ROWB) / 16) ^ (kk % GPR)) * 16;
+      const int kk = (wave * NREGW + i) * KPR + b16 / ROWB;   // key within the stage
+      loff[i] = i * 1024 + (b16 / ROWB) * ROWB + (((b16 % ROWB) / 16) ^ (kk % GPR)) * 16;
     } else {
-      const int vr = ri - NREG;
-      const int q0r = vr * QPR;                         // first token quad of the region
-      rblk[i] = (4 * q0r) / BS;
-      roff[i] = (q0r % (BS / 4)) * QB;
-      rdst[i] = KB + vr * VREG;
-      loff[i] = b16;
+      loff[i] = i * 1024 + b16;
     }
   }
 
-  // copies stage t into the buffer at byte offset boff; e: the table entries
-  // of its blocks.  A block past the context or with a bad entry reads
-  // block 0 (any valid address: its keys are masked and its V elements
-  // zeroed).
-  auto stage_copy = [&](int t, int boff, const int (&e)[BPS]) {
-    const char* blk[BPS];
-#pragma unroll
-    for (int bi = 0; bi < BPS; ++bi) {
-      uint32_t ph = (uint32_t)e[bi];
-      if (t * BPS + bi >= ctx_blocks) ph = 0;
-      else if (ph >= nb32) {                            // negative or past the pool
-        bad_entry = true;
-        ph = 0;
-      }
-      blk[bi] = cache + (int64_t)ph * block_stride;
+  // copies this wavefront's half of stage t into the buffer at byte offset
+  // boff; e: the table entry of its block.  A block past the context or with
+  // a bad entry reads block 0 (any valid address: its keys are masked and
+  // its V elements zeroed).
+  auto stage_copy = [&](int t, int boff, int e) {
+    uint32_t ph = (uint32_t)e;
+    if (t * BPS + wblk >= ctx_blocks) {
+      ph = 0;
+    } else if (ph >= nb32) {                          // negative or past the pool
+      bad_entry = true;
+      ph = 0;
     }
+    const char* base = cache + (int64_t)ph * block_stride + roff0;
 #pragma unroll
     for (int i = 0; i < NREGW; ++i) {
-      const char* src = blk[BPS == 1 ? 0 : rblk[i]] + roff[i] + loff[i];
-      char* dst = &s_kv[0][0] + boff + rdst[i];
+      const char* src = base + loff[i];
+      char* dst = &s_kv[0][0] + boff + rdst0 + i * rstep;
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   };
@@ -324,18 +323,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)s_ent[w & 1], 4,
                                      0, 0);
   };
-  // the entries of stage t (BPS <= 2), read from its window as one vector
-  typedef __attribute__((ext_vector_type(2))) int int2_t;
-  auto entries_read = [&](int t) -> int2_t {
-    const int32_t* w = s_ent[(t / SPW) & 1] + (t % SPW) * BPS;
-    if constexpr (BPS == 2) return *reinterpret_cast<const int2_t*>(w);
-    else return int2_t{w[0], 0};
-  };
-  // entries of stage t < 3, from those loaded up front
-  auto entries_pre = [&](int t, int (&e)[BPS]) {
-#pragma unroll
-    for (int bi = 0; bi < BPS; ++bi) e[bi] = epre[t * BPS + bi];
-  };
+  // the entry of this wavefront's block of stage t, read from its window
+  auto entries_read = [&](int t) -> int { return s_ent[(t / SPW) & 1][(t % SPW) * BPS + wblk]; };
+  // entry of stage t < 3, from those loaded up front
+  auto entries_pre = [&](int t) -> int { return epre[t]; };
 
   // ---- the products ----
   // Row limits are non-decreasing in the row, so the wavefront's valid rows
@@ -552,12 +543,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // and the loop (a load the compiler still counts as pending at the loop
   // entry would make every stage wait for all of its copies in flight; it
   // does not count the copies when it checks an explicit wait against Q).
-  int ecur[BPS];                                      // entries of stage t + 2
-  entries_pre(2, ecur);
+  int ecur = entries_pre(2);                          // entry of stage t + 2
   if (nstages > 0) {
-    int e0[BPS];
-    entries_pre(0, e0);
-    stage_copy(0, 0, e0);
+    stage_copy(0, 0, entries_pre(0));
     if (wave == 0 && nstages > 3) window_copy(0);
   }
 #pragma unroll
@@ -577,9 +565,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
       for (int cc = 0; cc < NQK; ++cc) qb[r][cc] ^= 0x80008000u;
   }
   if (nstages > 1) {
-    int e1[BPS];
-    entries_pre(1, e1);
-    stage_copy(1, STAGE, e1);
+    stage_copy(1, STAGE, entries_pre(1));
   }
 
   // Stage t is copied two stages ahead.  Waits are explicit (the barrier
@@ -591,7 +577,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // computes only the stages some row of it attends.  The buffers rotate:
   // stage t in buffer t % 3.
   int cb = 0, nb = 2 * STAGE;                         // byte offsets: compute, copy
-  int2_t ev = int2_t{0, 0};
+  int ev = 0;
   auto stage_begin = [&](int t) {
     if (t + 1 < nstages) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0 | NREGW);
@@ -604,8 +590,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (t > 0) {                                      // entries read in the last stage
-      ecur[0] = __builtin_amdgcn_readfirstlane(ev[0]);
-      if constexpr (BPS == 2) ecur[1] = __builtin_amdgcn_readfirstlane(ev[1]);
+      ecur = __builtin_amdgcn_readfirstlane(ev);
     }
     if (t + 2 < nstages) {
       // the window of stage t+4 when it opens one: its copy precedes this
@@ -636,14 +621,18 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     stage_end(t);
   }
 
-  // a row with no key gives zeros; a bad table entry NaN
+  // A bad table entry met by any wavefront (each checks the blocks it
+  // copies) makes the workgroup's rows NaN; a row with no key gives zeros.
+  s_bad[wave] = bad_entry ? 1 : 0;
+  __syncthreads();
+  const bool bad_any = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
   float4_t o[R][NPV];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float lt = l[r];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    const float inv = bad_entry ? __builtin_nanf("") : (lt > 0.0f ? p.v_scale / lt : 0.0f);
+    const float inv = bad_any ? __builtin_nanf("") : (lt > 0.0f ? p.v_scale / lt : 0.0f);
 #pragma unroll
     for (int jj = 0; jj < NPV; ++jj) o[r][jj] = acc[r][jj] * inv;
   }
