@@ -236,11 +236,11 @@ void decode_mfma_kernel(const DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
-      for (int i = 0; i < NKL; ++i) kd[u][i] = buffer_load16(rk, koff[u][i]);
+      for (int i = 0; i < NKL; ++i) kd[u][i] = stream_load16(rk, koff[u][i]);
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
-      for (int i = 0; i < NVL; ++i) vd[u][i] = buffer_load16(rv, voff[u][i]);
+      for (int i = 0; i < NVL; ++i) vd[u][i] = stream_load16(rv, voff[u][i]);
   };
 
   // Softmax state of head n, base 2.  m is the reference the weights are

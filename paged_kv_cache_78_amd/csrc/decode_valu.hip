@@ -296,9 +296,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + off, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i) kd[i] = buffer_load16(rk, lane * 16 + i * 1024);
+    for (int i = 0; i < NLOAD; ++i) kd[i] = stream_load16(rk, lane * 16 + i * 1024);
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i) vd[i] = buffer_load16(rv, lane * 16 + i * 1024);
+    for (int i = 0; i < NLOAD; ++i) vd[i] = stream_load16(rv, lane * 16 + i * 1024);
   };
 
   float m = kNegInf;       // reference max of this wavefront (wave-uniform)
