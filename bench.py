@@ -118,7 +118,7 @@ def cpu_baseline(wl, lens, budget_s: float = 10.0):
     table = wl.block_table.cpu().numpy()
     qn = to_numpy_bits(wl.q)
     i = 0
-    while t_total < budget_s and i < 4 * S:
+    while t_total < budget_s and i < 64 * S:
         s = order[i % S]
         i += 1
         L = int(lens[s])
