@@ -1,4 +1,5 @@
-"""The five workloads at full size, in the launch configuration bench.py
+"""The five decode workloads and the chunked-prefill workload at full size,
+in the launch configuration bench.py
 times (one decode step: the new tokens stored and attention over
 context_len + 1; one launch of pa_decode_append for the one-pass workloads,
 pa_cache_write + pa_decode_partitioned + pa_reduce for the long-context one),
@@ -74,3 +75,56 @@ def test_full_size_step_sampled(name, count):
         gv = to_numpy_bits(wl.v_cache[b, c["kvh"], o // 4, :, o % 4])
         assert gk.tobytes() == k_slot.tobytes(), (name, c["s"])
         assert gv.tobytes() == v_slot.tobytes(), (name, c["s"])
+
+
+def test_full_size_prefill_sampled():
+    """The chunked-prefill workload at full size (16 sequences x 512-token
+    chunks after up to 1536 cached tokens, Llama-7B shape), in the launch
+    configuration bench.py --op prefill times (pa_cache_write, then
+    pa_prefill): every output finite; sampled (sequence, head) pairs — all
+    512 query rows of each — against the oracle, which writes the chunk into
+    host copies of the sequence's own blocks of that kv head taken before
+    the step and attends over them."""
+    print("[full-size] llama7b_prefill_chunks", flush=True)
+    b = workloads.llama7b_prefill_chunks(device=DEV)
+    S, H, BS = b.num_seqs, b.num_heads, b.block_size
+    G = H // b.num_kv_heads
+    cu = b.cu_seqlens_q.cpu().numpy()
+    ctx = b.context_lens.cpu().numpy()
+    table = b.block_table.cpu().numpy()
+    slots = b.slot_mapping.cpu().numpy()
+    rng = np.random.default_rng(11)
+    seqs = [int(np.argmax(ctx)), int(np.argmin(ctx))] + [int(x) for x in rng.integers(0, S, 3)]
+    pairs = [(s, int(rng.integers(0, H))) for s in seqs]
+    captured = []
+    for s, h in pairs:
+        kvh = h // G
+        nblk = -(-int(ctx[s]) // BS)
+        ids = table[s, :nblk]
+        sel = torch.from_numpy(ids.astype(np.int64)).to(DEV)
+        rows = slice(int(cu[s]), int(cu[s + 1]))
+        # the chunk's slots inside the sequence's own blocks: block j of its table
+        pos = {int(p): j for j, p in enumerate(ids)}
+        sub = np.array([pos[int(x) // BS] * BS + int(x) % BS for x in slots[rows]], dtype=np.int32)
+        captured.append(dict(
+            s=s, h=h, nblk=nblk, sub_slots=sub, ctx=int(ctx[s]), n=int(cu[s + 1] - cu[s]),
+            q=to_numpy_bits(b.q[rows, h:h + 1]),
+            k=to_numpy_bits(b.k_cache.index_select(0, sel)[:, kvh:kvh + 1]),
+            v=to_numpy_bits(b.v_cache.index_select(0, sel)[:, kvh:kvh + 1]),
+            nk=to_numpy_bits(b.new_k[rows, kvh:kvh + 1]),
+            nv=to_numpy_bits(b.new_v[rows, kvh:kvh + 1])))
+    pa.cache_write(b.new_k, b.new_v, b.k_cache, b.v_cache, b.slot_mapping)
+    out = pa.prefill(b.q, b.k_cache, b.v_cache, b.block_table, b.cu_seqlens_q, b.context_lens,
+                     b.scale, b.max_seqlen_q)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    atol, rtol = tol_of(b)
+    for c in captured:
+        k, v = oracle.cache_write(c["nk"], c["nv"], c["k"], c["v"], c["sub_slots"], BS,
+                                  b.cache_dtype)
+        ref = oracle.paged_prefill(c["q"], k, v, np.arange(c["nblk"], dtype=np.int32)[None, :],
+                                   np.array([0, c["n"]], dtype=np.int32),
+                                   np.array([c["ctx"]], dtype=np.int32), b.scale, 1, BS,
+                                   b.q_dtype, b.cache_dtype)
+        got = as_f64(out[int(cu[c["s"]]):int(cu[c["s"] + 1]), c["h"]:c["h"] + 1])
+        assert_close(got, ref, atol, rtol, f"prefill sequence {c['s']} head {c['h']}")
