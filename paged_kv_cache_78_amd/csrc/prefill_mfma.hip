@@ -48,6 +48,11 @@
 #include "pa_decode_common.h"
 #include "pa_kernels.h"
 
+// LDS stage buffers of the prefill ring (3 or 4)
+#ifndef PA_PF_STAGES
+#define PA_PF_STAGES 3
+#endif
+
 namespace pa {
 namespace {
 
@@ -108,7 +113,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   constexpr int QB = Sh::QB, QPR = Sh::QPR, VREG = Sh::VREG, STAGE = Sh::STAGE;
   constexpr int NREGW = Sh::NREGW, ROWS = Sh::ROWS, TILE_BYTES = Sh::TILE_BYTES;
   constexpr int BPS = kPfKeys / BS;   // blocks per stage
-  constexpr int NST = 3;              // LDS ring: two stages in flight while one computes
+  constexpr int NST = PA_PF_STAGES;   // LDS ring: NST - 1 stages in flight while one computes
+  static_assert(NST == 3 || NST == 4, "stage ring");
   using M = Mma<QT>;
   using MV = std::conditional_t<ESZ == 1, Mma<F16>, Mma<QT>>;
   constexpr bool kSplitP = ESZ == 2 && __is_same(QT, BF16);
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // The sequence's lengths and the table entries of its first three stages
   // are loaded at once (indices clamped into the row; entries past the
   // context are never used), and waited for together before any branch.
-  constexpr int NPRE = 3;
+  constexpr int NPRE = NST;
   const int wblk = (16 * (wave & 1)) / BS;   // the stage block whose half this wavefront copies
   int epre[NPRE];
   const int32_t q0 = p.cu_seqlens_q[s];
@@ -311,9 +317,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   };
 
   // Table entries inside the loop come from LDS: windows of 64 entries are
-  // copied in by wavefront 0 into a ring of two, three stages before their
-  // first use (the copy stays clear of every wait until the next stage's,
-  // and a barrier publishes it).  Lane l copies the entry of block 64 w + l,
+  // copied in by wavefront 0 into a ring of two, 2 NST - 2 stages before their
+  // first use (the wait NST - 2 stages later covers the copy, and that
+  // stage's barrier publishes it).  Lane l copies the entry of block 64 w + l,
   // clamped into the context (entries past it are never used).  A scalar
   // load in flight would make every LDS wait of a stage wait for it too.
   constexpr int SPW = 64 / BPS;                       // stages per window
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   };
   // the entry of this wavefront's block of stage t, read from its window
   auto entries_read = [&](int t) -> int { return s_ent[(t / SPW) & 1][(t % SPW) * BPS + wblk]; };
-  // entry of stage t < 3, from those loaded up front
+  // entry of stage t < NST, from those loaded up front
   auto entries_pre = [&](int t) -> int { return epre[t]; };
 
   // ---- the products ----
@@ -343,7 +349,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // Logits are taken as raw products times |scale|: a negative scale flips
   // the sign of Q (exact), so the row maximum of the raw products scales to
   // the maximum of the logits.
-  const float sl = fabsf(p.qk_scale_log2);
+  // A zero scale takes the smallest normal instead: every logit is then
+  // below 2^-100 in magnitude, its weight exactly 1, and a masked product
+  // (-inf) still gives -inf.
+  const float sl = fmaxf(fabsf(p.qk_scale_log2), __FLT_MIN__);
 
   // running maximum starts finite, so that exp2(logit - m) needs no guard:
   // a masked logit (-inf) gives 0 whatever m is
@@ -418,41 +427,35 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     u32x4_t va[NPV];
 #pragma unroll
     for (int jj = 0; jj < NPV; ++jj) va[jj] = v_operand(vb, jj);
-    // Row maxima of the stage's logits, and the weights exp2(logit - m) taken
-    // at once with the running maximum m (recomputed in the rare stage that
-    // moves m, below), so the exponentials of one product chain overlap the
-    // matrix products of the others.
-    float mt[R], pr[R][8];
+    // Masked stage (some row of the wavefront stops inside it): products of
+    // keys past a row's limit become -inf, so their logits (times sl > 0)
+    // are -inf and their weights 0.  Then the row maxima of the stage.
     if (masked) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float x[8];
+      for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int key = key0 + 16 * (i >> 2) + 4 * g + (i & 3);
-          x[i] = key < lim[r] ? sc[r][i >> 2][i & 3] * sl : kNegInfP;
+          sc[r][i >> 2][i & 3] = key < lim[r] ? sc[r][i >> 2][i & 3] : kNegInfP;
         }
-        mt[r] = max8(x);
+    }
+    float mt[R];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pr[r][i] = exp2_hw(x[i] - m[r]);
-      }
-    } else {
+    for (int r = 0; r < R; ++r) {
+      float x[8];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = sc[r][i >> 2][i & 3];
-        mt[r] = max8(x) * sl;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pr[r][i] = exp2_hw(__builtin_fmaf(x[i], sl, -m[r]));
-      }
+      for (int i = 0; i < 8; ++i) x[i] = sc[r][i >> 2][i & 3];
+      mt[r] = max8(x) * sl;
     }
     bool grow = false;
 #pragma unroll
     for (int r = 0; r < R; ++r) grow |= mt[r] > m[r] + kSlackP;
     // Lazy rescale: the running maximum moves only when some row's stage
     // maximum passes it by more than the slack (weights stay below 2^slack);
-    // then the accumulators are rescaled and the stage's weights recomputed.
+    // then the accumulators are rescaled.  Decided before any weight is
+    // taken, so that the weights, their packing and the products that use
+    // them form one block: the products of one row block overlap the
+    // exponentials of the next.
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -465,30 +468,29 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         l[r] *= alpha;
 #pragma unroll
         for (int jj = 0; jj < NPV; ++jj) acc[r][jj] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int key = key0 + 16 * (i >> 2) + 4 * g + (i & 3);
-          pr[r][i] = key < lim[r] ? exp2_hw(__builtin_fmaf(sc[r][i >> 2][i & 3], sl, -m[r])) : 0.0f;
-        }
       }
     }
-    // the weights packed as the PV B operand, their sum, then the products
-    u32x4_t pb[R], pl[R];
+    // per row block: the weights exp2(logit - m), packed as the PV B
+    // operand, their sum, then the products
 #pragma unroll
     for (int r = 0; r < R; ++r) {
+      float pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pr[i] = exp2_hw(__builtin_fmaf(sc[r][i >> 2][i & 3], sl, -m[r]));
       uint32_t w[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) w[k] = MV::pack_pk(pr[r][2 * k], pr[r][2 * k + 1]);
-      pb[r] = u32x4_t{w[0], w[1], w[2], w[3]};
+      for (int k = 0; k < 4; ++k) w[k] = MV::pack_pk(pr[2 * k], pr[2 * k + 1]);
+      const u32x4_t pb = u32x4_t{w[0], w[1], w[2], w[3]};
+      u32x4_t pl = u32x4_t{0u, 0u, 0u, 0u};
       if constexpr (kSplitP) {
         uint32_t v2[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          v2[k] = MV::pack_pk(pr[r][2 * k] - MV::lo(w[k]), pr[r][2 * k + 1] - MV::hi(w[k]));
-        pl[r] = u32x4_t{v2[0], v2[1], v2[2], v2[3]};
+          v2[k] = MV::pack_pk(pr[2 * k] - MV::lo(w[k]), pr[2 * k + 1] - MV::hi(w[k]));
+        pl = u32x4_t{v2[0], v2[1], v2[2], v2[3]};
         float sum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sum += pr[r][i];
+        for (int i = 0; i < 8; ++i) sum += pr[i];
         l[r] += sum;
       } else {
         // the sum of the weights as they enter the product
@@ -497,14 +499,23 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         for (int k = 0; k < 4; ++k) lr = MV::sum2(w[k], lr);
         l[r] = lr;
       }
-    }
 #pragma unroll
-    for (int jj = 0; jj < NPV; ++jj) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        acc[r][jj] = MV::qk(va[jj], pb[r], acc[r][jj]);
-        if constexpr (kSplitP) acc[r][jj] = MV::qk(va[jj], pl[r], acc[r][jj]);
+      for (int jj = 0; jj < NPV; ++jj) {
+        acc[r][jj] = MV::qk(va[jj], pb, acc[r][jj]);
+        if constexpr (kSplitP) acc[r][jj] = MV::qk(va[jj], pl, acc[r][jj]);
       }
+    }
+    if constexpr (R == 2 && !kSplitP) {
+      // Order of the block above: the first row block's weights (8 fma, 8
+      // exp, 4 packs), then its 8 products each followed by 3 of the second
+      // row block's weight instructions, then the second row block's products.
+      __builtin_amdgcn_sched_group_barrier(0x402, 20, 0);
+#pragma unroll
+      for (int k = 0; k < NPV; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NPV, 0);
     }
   };
 
@@ -539,11 +550,11 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
   };
 
-  // Stage 0's copies, then Q, waited for together before stage 1's copies
+  // Stage 0's copies, then Q, waited for together before the next stages' copies
   // and the loop (a load the compiler still counts as pending at the loop
   // entry would make every stage wait for all of its copies in flight; it
   // does not count the copies when it checks an explicit wait against Q).
-  int ecur = entries_pre(2);                          // entry of stage t + 2
+  int ecur = entries_pre(NST - 1);                    // entry of stage t + NST - 1
   if (nstages > 0) {
     stage_copy(0, 0, entries_pre(0));
     if (wave == 0 && nstages > 3) window_copy(0);
@@ -564,22 +575,26 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int cc = 0; cc < NQK; ++cc) qb[r][cc] ^= 0x80008000u;
   }
-  if (nstages > 1) {
-    stage_copy(1, STAGE, entries_pre(1));
-  }
+#pragma unroll
+  for (int i = 1; i < NST - 1; ++i)
+    if (nstages > i) stage_copy(i, i * STAGE, entries_pre(i));
 
-  // Stage t is copied two stages ahead.  Waits are explicit (the barrier
-  // here is the bare instruction, whose implied fence would wait for every
-  // copy in flight): each lane waits for its own copies of stage t (those of
-  // stage t+1 may stay in flight) and for its LDS reads of stage t-1, then the
-  // barrier makes stage t complete for all and frees stage t-1's buffer, which
-  // receives stage t+2.  Every wavefront copies and meets every barrier; it
-  // computes only the stages some row of it attends.  The buffers rotate:
-  // stage t in buffer t % 3.
-  int cb = 0, nb = 2 * STAGE;                         // byte offsets: compute, copy
+  // Stage t is copied NST - 1 stages ahead.  Waits are explicit (the
+  // barrier here is the bare instruction, whose implied fence would wait for
+  // every copy in flight): each lane waits for its own copies of stage t
+  // (those of the next NST - 2 stages may stay in flight) and for its LDS
+  // reads of stage t-1, then the barrier makes stage t complete for all and
+  // frees stage t-1's buffer, which receives stage t + NST - 1.  Every
+  // wavefront copies and meets every barrier; it computes only the stages
+  // some row of it attends.  The buffers rotate: stage t in buffer t % NST.
+  // (Four buffers measured no faster than three: the copies arrive in time,
+  // and the waits at the barrier are the wavefronts waiting for each other.)
+  int cb = 0, nb = (NST - 1) * STAGE;                 // byte offsets: compute, copy
   int ev = 0;
   auto stage_begin = [&](int t) {
-    if (t + 1 < nstages) {
+    if (t + NST - 2 < nstages) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0 | ((NST - 2) * NREGW));
+    } else if (NST == 4 && t + 1 < nstages) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0 | NREGW);
     } else {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -592,19 +607,22 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     if (t > 0) {                                      // entries read in the last stage
       ecur = __builtin_amdgcn_readfirstlane(ev);
     }
-    if (t + 2 < nstages) {
-      // the window of stage t+4 when it opens one: its copy precedes this
-      // stage's copies, so the next stage's wait covers it
-      if (wave == 0 && t + 4 < nstages && (t + 4) % SPW == 0) window_copy((t + 4) / SPW);
-      stage_copy(t + 2, nb, ecur);
+    if (t + NST - 1 < nstages) {
+      // the window of stage t + 2 NST - 2 when it opens one: its copy
+      // precedes this stage's copies, so the wait NST - 2 stages on covers
+      // it, and the entries of its first stage are read at the end of that
+      // stage
+      constexpr int WA = 2 * NST - 2;
+      if (wave == 0 && t + WA < nstages && (t + WA) % SPW == 0) window_copy((t + WA) / SPW);
+      stage_copy(t + NST - 1, nb, ecur);
     }
   };
   auto stage_end = [&](int t) {
-    // entries of stage t+3, for the next stage's copy (its window arrived
-    // with this stage's barrier)
-    if (t + 3 < nstages) ev = entries_read(t + 3);
-    cb = cb == 2 * STAGE ? 0 : cb + STAGE;
-    nb = nb == 2 * STAGE ? 0 : nb + STAGE;
+    // entries of stage t + NST, for the next stage's copy (its window
+    // arrived with this stage's barrier)
+    if (t + NST < nstages) ev = entries_read(t + NST);
+    cb = cb == (NST - 1) * STAGE ? 0 : cb + STAGE;
+    nb = nb == (NST - 1) * STAGE ? 0 : nb + STAGE;
   };
   // The stages this wavefront computes come first, then those it only
   // copies (two loops, so that no path of the first leaves the accumulators

@@ -89,6 +89,19 @@ def test_grouped_heads_small_against_oracle(G):
     assert_close(as_f64(out), oracle_decode(wl), atol, rtol, f"G={G}")
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+@pytest.mark.parametrize("G", [1, 8])
+def test_negative_and_zero_scale(scale, G):
+    """A negative scale (logits change sign) and a zero scale (uniform
+    weights over the context), one head per kv head and grouped heads."""
+    wl = _small("f16" if G == 1 else "bf16", 128, 16, H=2 * G, KVH=2, lens=[1, 15, 16, 17, 99])
+    wl = workloads.synth.replace(wl, scale=scale)
+    out = _decode(_gpu(wl))
+    torch.cuda.synchronize()
+    atol, rtol = tol_of(wl)
+    assert_close(as_f64(out), oracle_decode(wl), atol, rtol, f"scale {scale} G={G}")
+
+
 # ----------------------------------------------------------------------------
 # identities that hold bit for bit
 

@@ -146,3 +146,13 @@ def test_bad_rows_are_nan():
     assert torch.all(torch.isnan(out[5:18]))
     ref, _, _ = _oracle_step(b)
     assert_close(out[:5].double().numpy(), ref[:5], *TOL["f16"], what="rows beside the bad ones")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_negative_and_zero_scale(scale, dtype):
+    """A negative scale (the logits change sign) and a zero scale (every key
+    of a row gets the same weight; masked keys still none)."""
+    b = workloads.prefill_batch(38, [9, 40, 1], [20, 0, 70], 8, 2, 128, 16, dtype)
+    b = workloads.synth.replace(workloads.poison_prefill(b), scale=scale)
+    _check(b, f"scale {scale} {dtype}")
