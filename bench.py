@@ -424,6 +424,27 @@ def bench_prefill(args, torch, pa, dev):
     }
 
 
+def measured_copy_gbs(torch, dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Bytes read + written per second by the best of `reps` plain device
+    copies of nbytes (the streaming-copy rate of this GPU, measured after the
+    timed region)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2 * nbytes / (best * 1e-3) / 1e9
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -593,6 +614,10 @@ def main(argv=None):
         },
         "cpu_baseline": cpu,
     }
+    if args.copy_calibration == 0:
+        copy_gbs = measured_copy_gbs(torch, dev)
+        rec["roofline"]["measured_copy_gbs"] = copy_gbs
+        rec["roofline"]["frac_of_measured_copy"] = achieved / copy_gbs
     print(json.dumps(rec))
     return 0
 
