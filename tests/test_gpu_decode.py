@@ -102,6 +102,30 @@ def test_negative_and_zero_scale(scale, G):
     assert_close(as_f64(out), oracle_decode(wl), atol, rtol, f"scale {scale} G={G}")
 
 
+@pytest.mark.parametrize("S,G", [(300, 1), (300, 8), (1100, 1), (1100, 4)])
+def test_many_sequences(S, G):
+    """More sequences than one lane set caches for the longest-first ranking
+    (256: lengths are read again in its second pass) and than the ranking
+    covers at all (1024: index order), one head per kv head and grouped;
+    sampled rows against the oracle, every row finite."""
+    if G == 1:
+        wl = workloads.llama7b_mha(seed=51, num_seqs=S, len_range=(0, 120), num_heads=2,
+                                   head_size=64, block_size=16)
+    else:
+        wl = workloads.gqa(seed=51, num_seqs=S, len_range=(0, 120), num_heads=2 * G,
+                           num_kv_heads=2, head_size=64, block_size=16)
+    print(f"[decode] {S} sequences, G={G}", flush=True)
+    g = _gpu(wl)
+    lens = (g.context_lens + 1).contiguous()
+    out = _decode(g, lens=lens)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    seqs = [0, 1, 255, 256, 257, S // 2, S - 1]
+    atol, rtol = tol_of(wl)
+    ref = oracle_decode(wl, lens=lens.cpu().numpy(), seqs=seqs)
+    assert_close(as_f64(out)[seqs], ref, atol, rtol, f"S={S} G={G}")
+
+
 # ----------------------------------------------------------------------------
 # identities that hold bit for bit
 
