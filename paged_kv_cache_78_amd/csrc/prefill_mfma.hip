@@ -509,13 +509,17 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
       // Order of the block above: the first row block's weights (8 fma, 8
       // exp, 4 packs), then its 8 products each followed by 3 of the second
       // row block's weight instructions, then the second row block's products.
-      __builtin_amdgcn_sched_group_barrier(0x402, 20, 0);
+      // Instruction classes of the scheduling groups: vector ALU including
+      // the transcendental unit (0x002 | 0x400), matrix core (0x008).
+      constexpr int kGroupValu = 0x002 | 0x400;
+      constexpr int kGroupMfma = 0x008;
+      __builtin_amdgcn_sched_group_barrier(kGroupValu, 20, 0);
 #pragma unroll
       for (int k = 0; k < NPV; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(kGroupMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kGroupValu, 3, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, NPV, 0);
+      __builtin_amdgcn_sched_group_barrier(kGroupMfma, NPV, 0);
     }
   };
 
