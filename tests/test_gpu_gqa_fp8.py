@@ -174,3 +174,20 @@ def test_grouped_short_contexts_with_spread_values(dtype):
     torch.cuda.synchronize()
     atol, rtol = tol_of(wl)
     assert_close(as_f64(out), oracle_decode(wl), atol, rtol, f"{dtype} short spread")
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_fp8_partitioned_against_oracle(G):
+    """fp8 e4m3fn caches through the split-context path (partials + reduce),
+    one head per kv head and grouped, with a shared prefix."""
+    wl = workloads.fp8_shared_prefix(seed=52, num_seqs=12, median=200.0, cap=700,
+                                     num_heads=2 * G, num_kv_heads=2, prefix_tokens=64)
+    wl = workloads.poison_unused_slots(wl)
+    print(f"[fp8 partitioned] G={G}", flush=True)
+    g = wl.to(DEV)
+    maxL = int(wl.context_lens.max())
+    out = pa.decode_partitioned(g.q, g.k_cache, g.v_cache, g.block_table, g.context_lens,
+                                wl.scale, 64, maxL, wl.k_scale, wl.v_scale)
+    torch.cuda.synchronize()
+    atol, rtol = tol_of(wl)
+    assert_close(as_f64(out), oracle_decode(wl), atol, rtol, f"fp8 partitioned G={G}")
