@@ -28,13 +28,13 @@ from .formats import (  # noqa: F401
     e4m3fn_to_f64,
     f16_to_f64,
     inv_scale_f32,
+    quantise_e4m3fn,
     to_f64,
 )
 from .paged_attention import (  # noqa: F401
     cache_write,
     decode_append,
     decode_sequence,
-    gather_kv,
     merge_partials,
     next_slot,
     num_logical_blocks,

@@ -111,3 +111,11 @@ def e4m3fn_encode(x: np.ndarray, inv_scale: np.float32) -> np.ndarray:
 def inv_scale_f32(scale: float) -> np.float32:
     """1/scale as one binary32 division (the cache writer's quantiser factor)."""
     return np.float32(np.float32(1.0) / np.float32(scale))
+
+
+def quantise_e4m3fn(x: np.ndarray, scale: float) -> np.ndarray:
+    """Codes an e4m3fn cache with per-tensor scale `scale` stores for the
+    values x (value = code * scale): the binary32 reciprocal of the scale is
+    taken once, each binary32 x is multiplied by it in binary32, and the
+    product is clamped and rounded to e4m3fn (e4m3fn_encode)."""
+    return e4m3fn_encode(np.asarray(x, dtype=np.float32), inv_scale_f32(scale))

@@ -44,7 +44,7 @@ from typing import List, Tuple
 
 import numpy as np
 
-from .formats import e4m3fn_encode, inv_scale_f32, to_f64
+from .formats import quantise_e4m3fn, to_f64
 
 
 # ----------------------------------------------------------------------------
@@ -102,21 +102,6 @@ def v_tiles_to_rows(vt: np.ndarray) -> np.ndarray:
     """V tiles [n, BS/4, D, 4] -> rows [n * BS, D] in token order."""
     n, q4, D, four = vt.shape
     return np.transpose(vt, (0, 1, 3, 2)).reshape(n * q4 * four, D)
-
-
-def gather_kv(k_cache: np.ndarray, v_cache: np.ndarray, block_table_row: np.ndarray,
-              context_len: int, block_size: int, kv_head: int):
-    """Contiguous fp64 K, V [L, D] of one sequence and kv head, read through
-    the block table.  k_cache/v_cache are fp64 (already dequantised)."""
-    L = int(context_len)
-    nblk = num_logical_blocks(L, block_size)
-    ids = np.asarray(block_table_row[:nblk], dtype=np.int64)
-    K = k_cache[ids, kv_head]                      # [nblk, BS, D]
-    V = v_cache[ids, kv_head]                      # [nblk, BS/4, D, 4]
-    D = K.shape[-1]
-    K = K.reshape(nblk * block_size, D)[:L]
-    V = v_tiles_to_rows(V)[:L]
-    return K, V
 
 
 def softmax_stats(x: np.ndarray):
@@ -269,12 +254,10 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, cache_fmt
     section 4.1, step 5: the token's K/V goes to its position inside the
     physical block); slot < 0 is skipped.  16-bit caches take the input bits
     unchanged; an e4m3fn cache takes e4m3fn(clamp(fp32(x) * fp32(1/scale)))
-    (see formats.e4m3fn_encode).  Inputs are not modified."""
+    (formats.quantise_e4m3fn).  Inputs are not modified."""
     kc = k_cache.copy()
     vc = v_cache.copy()
     NB = kc.shape[0]
-    k_inv = inv_scale_f32(k_scale)
-    v_inv = inv_scale_f32(v_scale)
     seen = set()
     for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
         if slot < 0:
@@ -286,8 +269,8 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, cache_fmt
         if b >= NB:
             raise ValueError(f"slot {slot} is outside the pool")
         if cache_fmt == "e4m3fn":
-            kk = e4m3fn_encode(to_f64(k[i], _fmt_of(k)).astype(np.float32), k_inv)
-            vv = e4m3fn_encode(to_f64(v[i], _fmt_of(v)).astype(np.float32), v_inv)
+            kk = quantise_e4m3fn(to_f64(k[i], _fmt_of(k)), k_scale)
+            vv = quantise_e4m3fn(to_f64(v[i], _fmt_of(v)), v_scale)
         else:
             kk, vv = k[i], v[i]
         kc[b, :, o, :] = kk
@@ -301,11 +284,11 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, block_size: int, cache_fmt
 def stored_rows(x, cache_fmt: str, scale: float = 1.0) -> np.ndarray:
     """fp64 values a cache of cache_fmt holds for new rows x (f16 or bf16
     bits), dequantised: 16-bit caches keep the input; e4m3fn caches hold
-    e4m3fn_encode(x, 1/scale), read back times scale."""
+    quantise_e4m3fn(x, scale), read back times scale."""
     xf = to_f64(x, _fmt_of(x))
     if cache_fmt != "e4m3fn":
         return xf
-    codes = e4m3fn_encode(xf.astype(np.float32), inv_scale_f32(scale))
+    codes = quantise_e4m3fn(xf, scale)
     return _dequant(codes, cache_fmt, scale)
 
 

@@ -76,14 +76,79 @@ def test_encode_matches_torch_cast_in_range():
     assert np.array_equal(enc, ref)
 
 
-def test_encode_saturates_and_applies_the_scale_in_binary32():
+def test_encode_saturates():
     big = np.array([449.0, 463.9, 464.0, 1e6, np.inf, -1e30], dtype=np.float32)
     enc = oracle.e4m3fn_encode(big, np.float32(1.0))
     assert list(enc) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
-    # the product is rounded to binary32 before the code is chosen
-    s = 0.1
-    inv = oracle.inv_scale_f32(s)
-    assert inv == np.float32(np.float32(1.0) / np.float32(0.1))
-    x = np.array([0.013, -0.7, 3.3], dtype=np.float32)
-    y = (x * inv).astype(np.float32)
-    assert np.array_equal(oracle.e4m3fn_encode(x, inv), oracle.e4m3fn_encode(y, np.float32(1.0)))
+
+
+def _f32(bits: int) -> np.float32:
+    return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+
+
+def test_quantiser_takes_the_binary32_reciprocal_and_a_binary32_product():
+    """Codes worked out by hand from the e4m3fn definition and binary32
+    rounding.  The quantiser's reading (the feature list names only "FP8 KV
+    cache"): code = e4m3fn(RNE(fp32(x * fp32(1 / fp32(scale))))).  Each case is
+    chosen so that dividing x by the scale, or keeping the reciprocal or the
+    product in fp64, lands on the other side of an e4m3fn rounding boundary.
+
+    Case A, scale 0.1:
+      fp32(0.1) = 0x3DCCCCCD = 0.100000001490116...; 1/that = 9.99999985098839,
+      which is 1.49e-7 below 10 while binary32 spacing in [8, 16) is 2^-20 =
+      9.5e-7, so fp32(1/scale) = 10 exactly.
+      x = 0x3F466666 = 0.77499997615814208984375; x * 10 = 7.75 - 2^-22
+      exactly, the midpoint between the binary32 neighbours 7.75 - 2^-21 and
+      7.75 (spacing 2^-21 in [4, 8)); ties-to-even picks 7.75 (0x40F80000,
+      even significand).  In e4m3fn, 7.75 is the midpoint of 7.5 (1.875 * 2^2,
+      mantissa 7, code 0x4F) and 8 (exponent field 10, mantissa 0, code 0x50);
+      ties-to-even gives 8: code 0x50.
+      Division: x / 0x3DCCCCCD = 7.7499996461..., 3.5e-7 below 7.75 (more than
+      half a spacing, 2^-22 = 2.4e-7), so binary32 keeps it below 7.75 (it
+      becomes 7.75 - 2^-21) -> 7.5 -> 0x4F.  An fp64
+      product x * 10 = 7.7499997615... is below 7.75 too -> 0x4F.
+
+    Case B, scale 0.3:
+      fp32(0.3) = 0x3E99999A = 0.300000011920928955078125; 1/that =
+      3.33333320087857...; the binary32 neighbours are 0x40555554 =
+      3.33333301544 and 0x40555555 = 3.33333325386, and the latter is nearer:
+      fp32(1/scale) = 3.3333332538604736.
+      x = 0x3F700001 = 0.9375 + 2^-24; x * 3.3333332538604736 = 3.12500023841...,
+      which binary32 rounds to 3.125 + 2^-22 (0x40480001), above the e4m3fn
+      midpoint 3.125 of 3.0 (code 0x44) and 3.25 (code 0x45): code 0x45.
+      Division: x / 0.3000000119 = 3.1250000745..., within half a spacing
+      (2^-23) of 3.125, so binary32 rounds it to the midpoint 3.125 itself and
+      ties-to-even gives 3.0 (mantissa 4) over 3.25 (mantissa 5): code 0x44.
+    """
+    inv_a = oracle.inv_scale_f32(0.1)
+    assert inv_a == np.float32(10.0)
+    assert oracle.quantise_e4m3fn(np.array([_f32(0x3F466666)]), 0.1)[0] == 0x50
+    assert oracle.quantise_e4m3fn(np.array([-_f32(0x3F466666)]), 0.1)[0] == 0xD0
+
+    inv_b = oracle.inv_scale_f32(0.3)
+    assert inv_b.view(np.uint32) == 0x40555555
+    assert oracle.quantise_e4m3fn(np.array([_f32(0x3F700001)]), 0.3)[0] == 0x45
+    # the same x with scale 1: 0.9375 + 2^-24 rounds to 0.9375 (code 0x37)
+    assert oracle.quantise_e4m3fn(np.array([_f32(0x3F700001)]), 1.0)[0] == 0x37
+
+
+def test_cache_write_fp8_code_of_a_bf16_value_at_a_rounding_boundary():
+    """One bf16 value through the oracle's cache write, scale 0.3, code worked
+    out by hand: x = bf16 0x3B90 = 1.125 * 2^-8 = 0.00439453125; times
+    fp32(1/0.3) = 3.3333332538604736 it is 0.0146484371507..., 3.5e-10 below
+    0.0146484375 = 15 * 2^-10 while binary32 spacing there is 2^-30 = 9.3e-10,
+    so the binary32 product is 0.0146484375 exactly: the midpoint of the
+    largest e4m3fn subnormal 7 * 2^-9 (code 0x07, odd mantissa) and the
+    smallest normal 2^-6 (code 0x08, even mantissa): code 0x08.  Dividing by
+    the scale gives 0.0146484369... < the midpoint, code 0x07."""
+    k = np.full((1, 1, 64), 0x3B90, dtype=np.uint16)
+    v = np.full((1, 1, 64), 0xBB90, dtype=np.uint16)                 # -x
+    kc = np.zeros((2, 1, 16, 64), dtype=np.uint8)
+    vc = np.zeros((2, 1, 4, 64, 4), dtype=np.uint8)
+    kc2, vc2 = oracle.cache_write(k, v, kc, vc, np.array([21], dtype=np.int32), 16, "e4m3fn",
+                                  k_scale=0.3, v_scale=0.3)
+    assert np.all(kc2[1, 0, 5] == 0x08)
+    assert np.all(vc2[1, 0, 1, :, 1] == 0x88)
+    kc2[1, 0, 5] = 0
+    vc2[1, 0, 1, :, 1] = 0
+    assert not kc2.any() and not vc2.any()

@@ -259,3 +259,36 @@ def test_block_manager_without_copy_on_write_is_caught(monkeypatch):
         return st["blocks"][j] * self.bs + pos % self.bs, None
     monkeypatch.setattr(bmod.BlockManager, "append_slot", append_in_place)
     assert _fails([t_bm.test_fork_shares_and_copy_on_write_splits])
+
+
+FP8_QUANTISER_PINS = [t_fp8.test_quantiser_takes_the_binary32_reciprocal_and_a_binary32_product,
+                      t_fp8.test_cache_write_fp8_code_of_a_bf16_value_at_a_rounding_boundary]
+
+
+def _patch_quantiser(monkeypatch, fn):
+    monkeypatch.setattr(fmt, "quantise_e4m3fn", fn)
+    monkeypatch.setattr(oracle, "quantise_e4m3fn", fn)
+    monkeypatch.setattr(pa_oracle, "quantise_e4m3fn", fn)
+
+
+def test_unmutated_quantiser_passes_its_pins():
+    assert not _fails(FP8_QUANTISER_PINS)
+
+
+def test_fp8_quantiser_that_divides_by_the_scale_is_caught(monkeypatch):
+    def divides(x, scale):
+        y = (np.asarray(x, dtype=np.float32) / np.float32(scale)).astype(np.float32)
+        return fmt.e4m3fn_encode(y, np.float32(1.0))
+    _patch_quantiser(monkeypatch, divides)
+    for pin in FP8_QUANTISER_PINS:
+        assert _fails([pin])
+
+
+def test_fp8_quantiser_with_fp64_reciprocal_and_product_is_caught(monkeypatch):
+    def fp64_product(x, scale):
+        y = np.asarray(x, dtype=np.float32).astype(np.float64) * (1.0 / float(np.float32(scale)))
+        flat = [fmt._e4m3fn_code_of_value(fmt.e4m3fn_round(float(t))) for t in y.reshape(-1)]
+        return np.array(flat, dtype=np.uint8).reshape(y.shape)
+    _patch_quantiser(monkeypatch, fp64_product)
+    for pin in FP8_QUANTISER_PINS:
+        assert _fails([pin])
