@@ -93,6 +93,12 @@ def lib() -> ctypes.CDLL:
     return L
 
 
+def _alloc(shape, dtype, device) -> torch.Tensor:
+    """Outputs and workspaces the binding allocates when the caller passes
+    none (uninitialised device memory)."""
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _check(status: int, what: str) -> None:
     if status != 0:
         msg = lib().pa_status_string(status).decode()
@@ -162,7 +168,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """One-pass paged decode attention; returns out [S, H, D] in q's dtype."""
     S, H, D, NB, KVH, BS = _decode_args(q, k_cache, v_cache, block_table, context_lens)
     if out is None:
-        out = torch.empty((S, H, D), dtype=q.dtype, device=q.device)
+        out = _alloc((S, H, D), q.dtype, q.device)
     _dev(out)
     _contig(out)
     _check(lib().pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
@@ -191,7 +197,7 @@ def decode_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cache: to
     if slot_mapping.numel() != S:
         raise PagedAttentionError("slot_mapping must hold one slot per sequence")
     if out is None:
-        out = torch.empty((S, H, D), dtype=q.dtype, device=q.device)
+        out = _alloc((S, H, D), q.dtype, q.device)
     _dev(out)
     _contig(out)
     _check(lib().pa_decode_append(
@@ -222,7 +228,7 @@ def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if cu_seqlens_q.numel() != S + 1 or block_table.shape[0] != S:
         raise PagedAttentionError("cu_seqlens_q must have num_seqs + 1 entries")
     if out is None:
-        out = torch.empty((T, H, D), dtype=q.dtype, device=q.device)
+        out = _alloc((T, H, D), q.dtype, q.device)
     _dev(out)
     _contig(out)
     _check(lib().pa_prefill(
@@ -267,9 +273,9 @@ def partition_workspace(num_seqs: int, num_heads: int, head_size: int, max_conte
     """(tmp_out [S, H, NP, D], max_logits [S, H, NP], exp_sums [S, H, NP]) fp32."""
     np_ = max(1, math.ceil(max_context_len / partition_size))
     f32 = torch.float32
-    return (torch.empty((num_seqs, num_heads, np_, head_size), dtype=f32, device=device),
-            torch.empty((num_seqs, num_heads, np_), dtype=f32, device=device),
-            torch.empty((num_seqs, num_heads, np_), dtype=f32, device=device))
+    return (_alloc((num_seqs, num_heads, np_, head_size), f32, device),
+            _alloc((num_seqs, num_heads, np_), f32, device),
+            _alloc((num_seqs, num_heads, np_), f32, device))
 
 
 def decode_partitioned_only(q, k_cache, v_cache, block_table, context_lens, scale,
@@ -311,7 +317,7 @@ def decode_partitioned(q, k_cache, v_cache, block_table, context_lens, scale,
     if workspace is None:
         workspace = partition_workspace(S, H, D, max_context_len, partition_size, q.device)
     if out is None:
-        out = torch.empty((S, H, D), dtype=q.dtype, device=q.device)
+        out = _alloc((S, H, D), q.dtype, q.device)
     decode_partitioned_only(q, k_cache, v_cache, block_table, context_lens, scale, partition_size,
                             max_context_len, workspace, k_scale, v_scale, stream)
     return reduce(out, workspace, context_lens, partition_size, stream)

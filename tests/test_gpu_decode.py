@@ -107,23 +107,23 @@ def test_many_sequences(S, G):
     """More sequences than one lane set caches for the longest-first ranking
     (256: lengths are read again in its second pass) and than the ranking
     covers at all (1024: index order), one head per kv head and grouped;
-    sampled rows against the oracle, every row finite."""
+    every row against the oracle (the output starts as NaN, so a sequence
+    the ranking skipped cannot pass)."""
     if G == 1:
         wl = workloads.llama7b_mha(seed=51, num_seqs=S, len_range=(0, 120), num_heads=2,
                                    head_size=64, block_size=16)
     else:
         wl = workloads.gqa(seed=51, num_seqs=S, len_range=(0, 120), num_heads=2 * G,
                            num_kv_heads=2, head_size=64, block_size=16)
+    wl = workloads.poison_unused_slots(wl, covered=(wl.context_lens + 1).tolist())
     print(f"[decode] {S} sequences, G={G}", flush=True)
     g = _gpu(wl)
     lens = (g.context_lens + 1).contiguous()
     out = _decode(g, lens=lens)
     torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all()
-    seqs = [0, 1, 255, 256, 257, S // 2, S - 1]
     atol, rtol = tol_of(wl)
-    ref = oracle_decode(wl, lens=lens.cpu().numpy(), seqs=seqs)
-    assert_close(as_f64(out)[seqs], ref, atol, rtol, f"S={S} G={G}")
+    ref = oracle_decode(wl, lens=lens.cpu().numpy())
+    assert_close(as_f64(out), ref, atol, rtol, f"S={S} G={G}, every row")
 
 
 # ----------------------------------------------------------------------------
