@@ -48,7 +48,8 @@
  * (pa_copy_blocks also takes pinned host memory) owned by the caller; inputs are only read; only out, the caches (pa_cache_write,
  * pa_decode_append, pa_copy_blocks) and
  * the workspace arrays are written.  The library allocates nothing and keeps
- * no state.  All calls are asynchronous on `stream` (a hipStream_t; NULL is
+ * no state, apart from the static scratch array of
+ * pa_decode_partitioned_noalloc.  All calls are asynchronous on `stream` (a hipStream_t; NULL is
  * the default stream); a PA_OK return means "launched", not "finished".
  *
  * Errors: arguments the host can check are checked before any launch and give
@@ -84,8 +85,10 @@ typedef enum {
   PA_ERR_HIP = -6,         /* the HIP runtime refused the launch            */
   PA_ERR_MEMORY = -7,      /* a pool is not device-accessible memory        */
   PA_ERR_NO_BLOCKS = -8,   /* block manager: not enough free blocks         */
-  PA_ERR_SEQUENCE = -9     /* block manager: unknown, duplicate or swapped-
+  PA_ERR_SEQUENCE = -9,    /* block manager: unknown, duplicate or swapped-
                               out sequence for this call                    */
+  PA_ERR_SCRATCH = -10     /* pa_decode_partitioned_noalloc: the partials do
+                              not fit in the library's static scratch       */
 } pa_status;
 
 /* Static text for a status code (never NULL). */
@@ -275,6 +278,35 @@ int pa_reduce(void* out, const float* tmp_out, const float* max_logits,
               const float* exp_sums, const int32_t* context_lens, int32_t num_seqs,
               int32_t num_heads, int32_t head_size, int32_t partition_size,
               int32_t max_num_partitions, pa_dtype out_dtype, void* stream);
+
+/*
+ * pa_decode_partitioned_noalloc — for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): pa_decode_partitioned followed by pa_reduce into out,
+ * with the partial triples kept in a static device array of the library
+ * (PA_NOALLOC_SCRATCH_BYTES per GPU, created when the library is loaded on
+ * that GPU and held until the process ends) instead of a caller workspace.
+ *   Arguments and result as pa_decode_partitioned + pa_reduce (out
+ *   [num_seqs, num_heads, head_size], q_dtype).  Calls no hipMalloc/hipFree.
+ *   The partials need S * H * NP * head_size * 4 bytes plus 2 * S * H * NP * 4
+ *   (NP = ceil(max_context_len / partition_size); each array rounded up to
+ *   256 bytes); more than PA_NOALLOC_SCRATCH_BYTES gives PA_ERR_SCRATCH and
+ *   nothing is launched, as does NP > 15360 (PA_ERR_WORKSPACE).
+ *   Every call on one GPU uses the same array: calls that overlap on one GPU
+ *   (different streams, or host threads) race and give wrong results; calls
+ *   ordered on one stream are safe.  Nothing in the array needs clearing:
+ *   the merge reads only partitions the same call wrote.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (48u << 20)
+int pa_decode_partitioned_noalloc(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* context_lens, float scale,
+                                  int32_t num_kv_heads, int32_t block_size, int32_t num_seqs,
+                                  int32_t num_heads, int32_t head_size,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  int64_t q_seq_stride, pa_dtype q_dtype, pa_dtype cache_dtype,
+                                  float k_scale, float v_scale, int32_t partition_size,
+                                  int32_t max_context_len, void* stream);
 
 /*
  * Host block manager (CPU code; no GPU call, no stream).  It decides where

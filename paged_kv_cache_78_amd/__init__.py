@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     decode,
     decode_append,
     decode_partitioned,
+    decode_partitioned_noalloc,
     decode_partitioned_only,
     lib,
     partition_workspace,

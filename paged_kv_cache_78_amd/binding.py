@@ -21,7 +21,7 @@ _DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_F
 
 EXPORTS = ("pa_status_string", "pa_abi_version", "pa_cache_write", "pa_decode",
            "pa_decode_append", "pa_prefill", "pa_copy_blocks", "pa_partition_workspace_bytes",
-           "pa_decode_partitioned", "pa_reduce", "pa_bm_create", "pa_bm_destroy",
+           "pa_decode_partitioned", "pa_reduce", "pa_decode_partitioned_noalloc", "pa_bm_create", "pa_bm_destroy",
            "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_append_slot", "pa_bm_append_slots",
            "pa_bm_free", "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_block_tables",
            "pa_bm_seq_len", "pa_bm_num_free", "pa_bm_ref_count")
@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
                                         vp, vp, vp, vp]
     L.pa_reduce.restype = ctypes.c_int
     L.pa_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    L.pa_decode_partitioned_noalloc.restype = ctypes.c_int
+    L.pa_decode_partitioned_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32,
+                                                i32, i32, i64, i64, ctypes.c_int, ctypes.c_int,
+                                                f32, f32, i32, i32, vp]
     P = ctypes.POINTER
     pi32, pi64 = P(i32), P(i64)
     L.pa_bm_create.restype = vp
@@ -321,6 +325,25 @@ def decode_partitioned(q, k_cache, v_cache, block_table, context_lens, scale,
     decode_partitioned_only(q, k_cache, v_cache, block_table, context_lens, scale, partition_size,
                             max_context_len, workspace, k_scale, v_scale, stream)
     return reduce(out, workspace, context_lens, partition_size, stream)
+
+
+def decode_partitioned_noalloc(q, k_cache, v_cache, block_table, context_lens, scale,
+                               partition_size: int, max_context_len: int, out: torch.Tensor,
+                               k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """pa_decode_partitioned_noalloc: partitioned decode and merge into the
+    caller's out, the partials in the library's static scratch (no device
+    allocation by the library or here: out is required)."""
+    S, H, D, NB, KVH, BS = _decode_args(q, k_cache, v_cache, block_table, context_lens)
+    _dev(out)
+    _contig(out)
+    if tuple(out.shape) != (S, H, D) or out.dtype != q.dtype:
+        raise PagedAttentionError("out must be [S, H, D] in q's dtype")
+    _check(lib().pa_decode_partitioned_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
+        scale, KVH, BS, S, H, D, block_table.shape[1], NB, q.stride(0), _DT[q.dtype],
+        _DT[k_cache.dtype], k_scale, v_scale, partition_size, max_context_len,
+        _stream(stream)), "pa_decode_partitioned_noalloc")
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -153,11 +153,12 @@ const char* pa_status_string(int status) {
     case PA_ERR_MEMORY: return "a pointer is not device-accessible memory (device, managed or pinned host)";
     case PA_ERR_NO_BLOCKS: return "not enough free blocks";
     case PA_ERR_SEQUENCE: return "unknown, duplicate or swapped-out sequence for this call";
+    case PA_ERR_SCRATCH: return "the partial results exceed the library's static scratch array";
     default: return "unknown status";
   }
 }
 
-int pa_abi_version(void) { return 2; }
+int pa_abi_version(void) { return 3; }
 
 int pa_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
                    const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,

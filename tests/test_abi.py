@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(pa.EXPORTS) == set(_declared())
-    assert L.pa_abi_version() == 2
+    assert L.pa_abi_version() == 3
     assert L.pa_status_string(0) == b"ok"
     assert L.pa_status_string(-3).startswith(b"head size")
 
