@@ -20,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
+PROBE = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 ARCH = "gfx950"
 
 
@@ -46,8 +48,8 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(os.path.basename(src))[0] + ".o")
+def _compile(src: str, tag: str = "") -> str:
+    obj = os.path.join(OBJ, tag + os.path.splitext(os.path.basename(src))[0] + ".o")
     if src.endswith(".cpp"):
         cmd = [shutil.which("g++") or "g++", *HOST, "-c", src, "-o", obj]
     else:
@@ -58,12 +60,8 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     # every symbol resolved at link time: a kernel whose launch stub the host
     # pass failed to emit must fail the build, not the first load
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp,
@@ -71,9 +69,22 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """libpa.so (the library) and libpa_probe.so (the streaming probe bench.py
+    reads the HBM ceiling with)."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sources()
+    probe_srcs = sorted(os.path.join(PROBE, f) for f in os.listdir(PROBE) if f.endswith(".hip"))
+    jobs = [(s, "") for s in srcs] + [(s, "probe_") for s in probe_srcs]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
