@@ -72,7 +72,13 @@ extern "C" {
 typedef enum {
   PA_F16 = 0,
   PA_BF16 = 1,
-  PA_FP8_E4M3FN = 2
+  PA_FP8_E4M3FN = 2,
+  /* Range markers, never valid element types: they make every int32 value a
+   * value of pa_dtype, so that a call passing an unknown type is rejected
+   * with PA_ERR_DTYPE rather than reading an out-of-range enum (undefined
+   * in C++).  The type stays int-sized. */
+  PA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  PA_DTYPE_RANGE_MAX_ = 2147483647
 } pa_dtype;
 
 typedef enum {

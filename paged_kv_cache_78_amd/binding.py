@@ -13,7 +13,10 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+# PA_LIB names another build of the same library (the host-sanitizer build
+# of the CPU tests); by default the in-tree libpa.so
+_LIB_PATH = os.environ.get("PA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                      "libpa.so")
 _lib = None
 
 PA_F16, PA_BF16, PA_FP8_E4M3FN = 0, 1, 2

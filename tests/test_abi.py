@@ -66,7 +66,7 @@ def _decode(**kw):
     (dict(v=ctypes.c_void_p(0x1004)), -2),
     (dict(d=96, qs=384), -3), (dict(bs=8), -3), (dict(h=64, kvh=2, qs=64 * 128), -3),
     (dict(qt=2), -4), (dict(qt=0, ct=1), -4), (dict(ct=2, ks=0.0), -4),
-    (dict(ct=2, vs=float("inf")), -4),
+    (dict(ct=2, vs=float("inf")), -4), (dict(qt=-1), -4), (dict(ct=99), -4),
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
@@ -145,7 +145,7 @@ def _copy(**kw):
     (dict(sk=None), -1), (dict(dv=None), -1), (dict(m=None), -1),
     (dict(n=-1), -2), (dict(n=70000), -2), (dict(snb=0), -2), (dict(kvh=0), -2),
     (dict(dk=ctypes.c_void_p(0x1008)), -2),
-    (dict(d=96), -3), (dict(bs=8), -3), (dict(ct=7), -4),
+    (dict(d=96), -3), (dict(bs=8), -3), (dict(ct=7), -4), (dict(ct=-1), -4),
 ])
 def test_copy_blocks_rejects(kw, status):
     assert _copy(**kw) == status
