@@ -759,6 +759,7 @@ def main(argv=None):
         "flushed": head["flushed"],
         "cpu_baseline": head["cpu_baseline"],
         "stream_ceiling": ceiling,
+        "library": os.path.relpath(pa.binding._LIB_PATH, ROOT),
         "per_config": per,
     }
     print(json.dumps(rec))

@@ -22,6 +22,15 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 PROBE = os.path.join(PKG, "probe")
 PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
+# Build-flag variants of the decode kernels, kept for measurement: the same
+# library with only the decode kernel files rebuilt under the flag.  Load one
+# with PA_LIB=paged_kv_cache_78_amd/variants/libpa_<name>.so.
+#   xlane_dpp: cross-lane reductions on DPP and v_permlane*_swap instead of
+#              ds_bpermute;
+#   table_lds: block-table window staged through LDS instead of v_readlane.
+VARIANTS = {"xlane_dpp": ["-DPA_XLANE_DPP=1"], "table_lds": ["-DPA_TABLE_LDS=1"]}
+VARIANT_FILES = ("decode_valu.hip", "decode_mfma.hip")
+VARIANT_DIR = os.path.join(PKG, "variants")
 ARCH = "gfx950"
 
 
@@ -48,12 +57,12 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src: str, tag: str = "") -> str:
+def _compile(src: str, tag: str = "", extra=()) -> str:
     obj = os.path.join(OBJ, tag + os.path.splitext(os.path.basename(src))[0] + ".o")
     if src.endswith(".cpp"):
         cmd = [shutil.which("g++") or "g++", *HOST, "-c", src, "-o", obj]
     else:
-        cmd = [_hipcc(), *COMMON, "-c", src, "-o", obj]
+        cmd = [_hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -78,13 +87,25 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sources()
     probe_srcs = sorted(os.path.join(PROBE, f) for f in os.listdir(PROBE) if f.endswith(".hip"))
-    jobs = [(s, "") for s in srcs] + [(s, "probe_") for s in probe_srcs]
+    jobs = [(s, "", ()) for s in srcs] + [(s, "probe_", ()) for s in probe_srcs]
+    var_srcs = [s for s in srcs if os.path.basename(s) in VARIANT_FILES]
+    for name, flags in VARIANTS.items():
+        jobs += [(s, name + "_", tuple(flags)) for s in var_srcs]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
-    _link(objs[:len(srcs)], LIB)
-    _link(objs[len(srcs):], PROBE_LIB)
+    base = objs[:len(srcs)]
+    _link(base, LIB)
+    _link(objs[len(srcs):len(srcs) + len(probe_srcs)], PROBE_LIB)
+    os.makedirs(VARIANT_DIR, exist_ok=True)
+    k = len(srcs) + len(probe_srcs)
+    for name in VARIANTS:
+        own = objs[k:k + len(var_srcs)]
+        k += len(var_srcs)
+        swap = dict(zip(var_srcs, own))
+        _link([swap.get(s, o) for s, o in zip(srcs, base)],
+              os.path.join(VARIANT_DIR, f"libpa_{name}.so"))
     if verbose:
-        print(f"built {LIB} and {PROBE_LIB}")
+        print(f"built {LIB}, {PROBE_LIB} and the variants in {VARIANT_DIR}")
     return LIB
 
 

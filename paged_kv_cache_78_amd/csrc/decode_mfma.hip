@@ -82,6 +82,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   __shared__ int s_hist[PART ? 1 : WAVES * kSchedKeys];
   __shared__ float s_state[WAVES > 1 ? (WAVES - 1) * kWave * NSTATE : 1];
   __shared__ __attribute__((aligned(16))) float s_new[PART ? 4 : 2 * D];   // fused append
+  __shared__ int s_table[table_lds_ints(WAVES)];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;          // head column / token row of the products
@@ -200,8 +201,9 @@ void decode_mfma_kernel(const DecodeParams p) {
   const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)kvh * TILE_BYTES;
   const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE_BYTES;
   const int64_t block_stride = (int64_t)KVH * TILE_BYTES;
-  TableWindow tw;
-  tw.init(p.block_table + (int64_t)s * MB + my_first, ntiles, p.num_blocks, lane);
+  TableSlice tw;
+  tw.init(p.block_table + (int64_t)s * MB + my_first, ntiles, p.num_blocks, lane,
+          s_table + wave * kWave);
 
   // per-lane byte offsets inside a tile
   uint32_t koff[SUB][NKL];
@@ -299,8 +301,7 @@ void decode_mfma_kernel(const DecodeParams p) {
       if (__builtin_amdgcn_ballot_w64(mt > m + kSlack) != 0) {
         // raise each head's reference to the larger of it and this
         // sub-tile's max (earlier logits stay within kSlack of it)
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = xor_max<32>(xor_max<16>(mt));
         const float mn = fmaxf(m, mt);
         const float alpha = (m == mn) ? 1.0f : exp2_hw(m - mn);
         m = mn;
@@ -367,8 +368,7 @@ void decode_mfma_kernel(const DecodeParams p) {
         xn = fmaf(M::hi(qb[c][w]), kk[2 * w + 1], xn);
       }
     }
-    xn += __shfl_xor(xn, 16, 64);
-    xn += __shfl_xor(xn, 32, 64);
+    xn = xor_add<32>(xor_add<16>(xn));
     m = xn * p.qk_scale_log2;            // reference = its logit: weight 1
     mx = m;
     l = (g == 0) ? 1.0f : 0.0f;          // the four lane groups' sums add up
@@ -402,7 +402,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
   }
 
-  bool bad = tw.bad;
+  bool bad = table_bad(tw);
   if constexpr (WAVES > 1) {
     // merge the wavefronts' states (each with its own reference max)
     if (wave > 0) {
@@ -438,10 +438,8 @@ void decode_mfma_kernel(const DecodeParams p) {
 
   // the normaliser of head n: sum over the four lane groups; the partial
   // triple reports the exact max, with the sum re-referenced to it
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  l = xor_add<32>(xor_add<16>(l));
+  mx = xor_max<32>(xor_max<16>(mx));
 
   float4_t o[NPV];
   const float nanv = __builtin_nanf("");

@@ -151,12 +151,6 @@ __device__ __forceinline__ void v_chunk(const u32x4_t& w, float (&out)[E][4]) {
   }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
-}
-
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kSlack = 8.0f;   // weights stay <= 2^8 between reference moves
 
@@ -180,6 +174,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   __shared__ int s_hist[PART ? 1 : WAVES * kSchedKeys];
   __shared__ float s_state[WAVES > 1 ? (WAVES - 1) * kWave * NSTATE : 1];
   __shared__ __attribute__((aligned(16))) float s_new[PART ? 4 : 2 * D];   // fused append
+  __shared__ int s_table[table_lds_ints(WAVES)];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int lane = threadIdx.x & 63;
@@ -279,8 +274,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)kvh * TILE_BYTES;
   const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE_BYTES;
   const int64_t block_stride = (int64_t)p.num_kv_heads * TILE_BYTES;
-  TableWindow tw;
-  tw.init(p.block_table + (int64_t)s * MB + my_first, ntiles, p.num_blocks, lane);
+  TableSlice tw;
+  tw.init(p.block_table + (int64_t)s * MB + my_first, ntiles, p.num_blocks, lane,
+          s_table + wave * kWave);
 
   u32x4_t kb[NBUF][NLOAD];
   u32x4_t vb[NBUF][NLOAD];
@@ -415,14 +411,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   // lanes sharing head dims add up (one reference max); the weight sum adds
   // one lane per K token row
 #pragma unroll
-  for (int o = LPQ; o < kWave; o <<= 1) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
-  }
-#pragma unroll
-  for (int o = LPT; o < kWave; o <<= 1) l += __shfl_xor(l, o, kWave);
+  for (int e = 0; e < E; ++e) acc[e] = sum_lanes_mod<LPQ>(acc[e]);
+  l = sum_lanes_mod<LPT>(l);
 
-  bool bad = tw.bad;
+  bool bad = table_bad(tw);
   if constexpr (WAVES > 1) {
     // merge the wavefronts' states (lane i holds the same dims in every one)
     if (wave > 0) {

@@ -40,6 +40,9 @@ struct TableWindow {
     cur = sanitize(0, lane, raw(0, lane));
     nxt = raw(64, lane);
   }
+  __device__ __forceinline__ void init(const int32_t* slice, int n, int64_t nb, int lane, int*) {
+    init(slice, n, nb, lane);
+  }
   // Physical block of tile t (wave-uniform, t < ntiles, called with t
   // increasing by one).
   __device__ __forceinline__ int phys(int t, int lane) {
@@ -51,6 +54,48 @@ struct TableWindow {
     return __builtin_amdgcn_readlane(cur, t - cbase);
   }
 };
+
+// The same window staged through LDS: each chunk of 64 entries is loaded as
+// above (one per lane, the next chunk a chunk ahead), checked, written to the
+// wavefront's 64-entry LDS slice, and every tile reads its entry back with one
+// LDS load at a wave-uniform address.  Built with PA_TABLE_LDS=1 so that
+// bench.py can compare it with the register window.
+struct TableLds {
+  TableWindow w;
+  int* s;
+
+  __device__ __forceinline__ void init(const int32_t* slice, int n, int64_t nb, int lane,
+                                       int* lds) {
+    w.init(slice, n, nb, lane);
+    s = lds;
+    s[lane] = w.cur;
+    __builtin_amdgcn_wave_barrier();
+  }
+  __device__ __forceinline__ int phys(int t, int lane) {
+    if (t - w.cbase == 64) {
+      w.cbase += 64;
+      w.cur = w.sanitize(w.cbase, lane, w.nxt);
+      w.nxt = w.raw(w.cbase + 64, lane);
+      __builtin_amdgcn_wave_barrier();
+      s[lane] = w.cur;
+      __builtin_amdgcn_wave_barrier();
+    }
+    return __builtin_amdgcn_readfirstlane(s[t - w.cbase]);
+  }
+};
+
+#ifndef PA_TABLE_LDS
+#define PA_TABLE_LDS 0
+#endif
+#if PA_TABLE_LDS
+using TableSlice = TableLds;
+__device__ __forceinline__ bool table_bad(const TableLds& t) { return t.w.bad; }
+#else
+using TableSlice = TableWindow;
+__device__ __forceinline__ bool table_bad(const TableWindow& t) { return t.bad; }
+#endif
+// LDS the table slices of a workgroup of `waves` wavefronts take (ints)
+constexpr int table_lds_ints(int waves) { return PA_TABLE_LDS ? waves * kWave : 1; }
 
 // Longest-first order of sequences, computed by every workgroup of a
 // one-pass launch from context_lens alone (no workspace, no host sync).

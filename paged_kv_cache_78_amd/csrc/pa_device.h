@@ -89,6 +89,96 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// ---------------------------------------------------------------------------
+// Reductions across lanes further apart than a quad.  Default build: the
+// exchanges go through ds_bpermute (__shfl_xor), an LDS-unit instruction.
+// PA_XLANE_DPP=1 builds them from DPP row operations and gfx950's
+// v_permlane16_swap / v_permlane32_swap (no LDS instruction); bench.py can
+// load that build to compare the two.
+
+#ifndef PA_XLANE_DPP
+#define PA_XLANE_DPP 0
+#endif
+
+#if PA_XLANE_DPP
+// The values of lanes l and l ^ O (O = 16 or 32), in both lanes of the pair:
+// v_permlane{16,32}_swap exchanges the odd 16- (32-) lane rows of its first
+// register with the even rows of its second, so with x in both, the first
+// ends up holding the even rows' values and the second the odd rows'.  Both
+// registers are written; written as inline assembly because this compiler's
+// builtin returns the first register twice (a lane-layout probe on the GPU
+// showed it).  The compiler does not insert the wait states around inline
+// assembly that it inserts around its own permlane instructions, so the
+// s_nops provide them on both sides.
+template <int O>
+__device__ __forceinline__ float2_t pair_values(float x) {
+  static_assert(O == 16 || O == 32, "distance");
+  int a = __builtin_bit_cast(int, x), b = a;
+  if constexpr (O == 32)
+    asm("s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 4" : "+v"(a), "+v"(b));
+  else
+    asm("s_nop 4\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 4" : "+v"(a), "+v"(b));
+  return float2_t{__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)};
+}
+#endif
+
+// x + (x of lane l ^ O), O in {4, 8, 16, 32}, the same in both lanes of the
+// pair.  (For O = 4 the DPP build adds lane (l + 4) mod 16 instead, which
+// gives the same totals once O = 8 follows.)
+template <int O>
+__device__ __forceinline__ float xor_add(float x) {
+#if PA_XLANE_DPP
+  if constexpr (O == 4 || O == 8) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             0, __builtin_bit_cast(int, x), 0x120 + O, 0xF, 0xF,
+                                             false));
+  } else {
+    const float2_t v = pair_values<O>(x);
+    return v[0] + v[1];
+  }
+#else
+  return x + __shfl_xor(x, O, kWave);
+#endif
+}
+
+// max(x, x of lane l ^ O), O in {16, 32}.
+template <int O>
+__device__ __forceinline__ float xor_max(float x) {
+#if PA_XLANE_DPP
+  const float2_t v = pair_values<O>(x);
+  return fmaxf(v[0], v[1]);
+#else
+  return fmaxf(x, __shfl_xor(x, O, kWave));
+#endif
+}
+
+// Maximum over the whole wavefront, in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+#if PA_XLANE_DPP
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
+  return xor_max<32>(xor_max<16>(x));
+#else
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+#endif
+}
+
+// Sum over the lanes that share lane % O (O in {4, 8, 16, 32, 64}; 64: x).
+template <int O>
+__device__ __forceinline__ float sum_lanes_mod(float x) {
+  static_assert(O >= 4, "distance");
+  if constexpr (O >= kWave) return x;
+  else return sum_lanes_mod<2 * O>(xor_add<O>(x));
+}
+
 // Value of lane (lane ^ M) for M in {1, 2} (quad permutes).
 template <int M>
 __device__ __forceinline__ float xor_lane(float x) {
