@@ -448,25 +448,28 @@ class StreamProbe:
         self.lib = ctypes.CDLL(path)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         self.lib.pa_probe_stream.restype = ctypes.c_int
-        self.lib.pa_probe_stream.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp]
+        self.lib.pa_probe_stream.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, vp, vp]
         self.ctypes = ctypes
 
-    def launch(self, torch, pool, num_tiles, ids, num_waves, tiles_per_wave, nontemporal, sink):
+    def launch(self, torch, pool, num_tiles, ids, num_waves, tiles_per_wave, nontemporal, sink,
+               tile_bytes=4096, in_flight=3):
         c = self.ctypes
         st = self.lib.pa_probe_stream(c.c_void_p(pool.data_ptr()), num_tiles,
                                       c.c_void_p(ids.data_ptr()), num_waves, tiles_per_wave,
-                                      1 if nontemporal else 0, c.c_void_p(sink.data_ptr()),
+                                      tile_bytes, in_flight, 1 if nontemporal else 0,
+                                      c.c_void_p(sink.data_ptr()),
                                       c.c_void_p(torch.cuda.current_stream().cuda_stream))
         if st != 0:
             raise RuntimeError(f"pa_probe_stream failed ({st})")
 
 
 def stream_rate(torch, probe, dev, pool_bytes: int, num_waves: int, tiles_per_wave: int,
-                nontemporal: bool, reps: int = 5, seed: int = 9) -> dict:
+                nontemporal: bool, reps: int = 5, seed: int = 9, tile_bytes: int = 4096,
+                in_flight: int = 3) -> dict:
     """GB/s read by the probe: num_waves wavefronts x tiles_per_wave distinct
-    random 4 KiB tiles of a pool_bytes pool (best and median of reps launches
-    after one warm-up)."""
-    num_tiles = pool_bytes // 4096
+    random tiles of tile_bytes of a pool_bytes pool, in_flight tiles in flight
+    per wavefront (best and median of reps launches after one warm-up)."""
+    num_tiles = pool_bytes // tile_bytes
     need = num_waves * tiles_per_wave
     assert need <= num_tiles
     g = torch.Generator(device=dev)
@@ -474,39 +477,49 @@ def stream_rate(torch, probe, dev, pool_bytes: int, num_waves: int, tiles_per_wa
     pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
     ids = torch.randperm(num_tiles, generator=g, device=dev)[:need].to(torch.int32).contiguous()
     sink = torch.empty(num_waves * 64, dtype=torch.int32, device=dev)
-    probe.launch(torch, pool, num_tiles, ids, num_waves, tiles_per_wave, nontemporal, sink)
+    args = (torch, pool, num_tiles, ids, num_waves, tiles_per_wave, nontemporal, sink, tile_bytes,
+            in_flight)
+    probe.launch(*args)
     ms = []
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        probe.launch(torch, pool, num_tiles, ids, num_waves, tiles_per_wave, nontemporal, sink)
+        probe.launch(*args)
         e1.record()
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
     del pool, ids, sink
-    b = need * 4096
+    b = need * tile_bytes
     ms.sort()
     return {"best_gbs": b / (ms[0] * 1e-3) / 1e9, "median_gbs": b / (ms[len(ms) // 2] * 1e-3) / 1e9,
             "bytes": b, "num_waves": num_waves, "tiles_per_wave": tiles_per_wave,
-            "nontemporal": nontemporal}
+            "tile_bytes": tile_bytes, "in_flight": in_flight, "nontemporal": nontemporal}
 
 
 def bench_stream(args, torch, dev):
-    """The probe over a few launch shapes and both cache policies."""
+    """The probe over launch shapes, tile sizes (4 KiB: a 16-bit K or V tile
+    at block 16, head 128; 2 KiB: the same in fp8), tiles in flight and both
+    cache policies."""
     probe = StreamProbe()
     rows = []
     for nt in (True, False):
         for waves, tiles in ((2048, 64), (8192, 16), (8192, 32), (16384, 16)):
             rows.append(stream_rate(torch, probe, dev, 8 << 30, waves, tiles, nt))
+    for tb in (4096, 2048):
+        for fl in (2, 3, 4, 6, 8):
+            rows.append(stream_rate(torch, probe, dev, 8 << 30, 8192, 32 * 4096 // tb, True,
+                                    tile_bytes=tb, in_flight=fl))
+    rows.append(stream_rate(torch, probe, dev, 8 << 30, 12288, 32, True, tile_bytes=2048,
+                            in_flight=4))
     best = max(r["best_gbs"] for r in rows if r["nontemporal"])
     return {
         "metric": "HBM read GB/s of random 4 KiB tiles streamed like the decode kernels, 1×MI355X",
         "value": best, "unit": "GB/s", "n_gpus": 1, "steps": 5, "warmup": 1,
         "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u8", "data": "synthetic",
-        "config": {"workload": "stream probe: distinct random 4 KiB tiles of an 8 GiB pool, "
-                               "3 tiles in flight per wavefront", "sweep": rows},
+        "config": {"workload": "stream probe: distinct random 2 or 4 KiB tiles of an 8 GiB pool",
+                   "sweep": rows},
         "roofline": {"bound": "hbm", "achieved": best, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": best / PEAK_HBM_GBS, "traffic": None},
         "cpu_baseline": None,

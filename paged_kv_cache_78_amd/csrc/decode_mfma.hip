@@ -42,6 +42,13 @@
 #ifndef PA_MFMA_NBUF
 #define PA_MFMA_NBUF 3
 #endif
+// fp8 caches: tiles in flight per wavefront and wavefronts per SIMD
+#ifndef PA_MFMA_NBUF_FP8
+#define PA_MFMA_NBUF_FP8 3
+#endif
+#ifndef PA_MFMA_FP8_WAVES_PER_EU
+#define PA_MFMA_FP8_WAVES_PER_EU 3
+#endif
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
 #endif
@@ -55,7 +62,7 @@ constexpr float kNegInf = kMfmaNegInf;
 // need the register budget of two), and the extra wavefronts keep more tiles
 // in flight per compute unit.
 template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(CT::kBytes == 1 ? 3 : 1)))
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(CT::kBytes == 1 ? PA_MFMA_FP8_WAVES_PER_EU : 1)))
 void decode_mfma_kernel(const DecodeParams p) {
   constexpr int ESZ = CT::kBytes;
   constexpr int SUB = BS / 16;              // 16-token sub-tiles per block
@@ -65,7 +72,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   constexpr int E = 16 / (4 * ESZ);         // head dims per 16-byte V load (4 tokens each)
   constexpr int NVL = NPV / E;              // 16-byte V loads per sub-tile
   constexpr int NKL = ESZ == 2 ? NQK : NQK / 2;   // 16-byte K loads per sub-tile
-  constexpr int NBUF = PA_MFMA_NBUF;
+  constexpr int NBUF = ESZ == 1 ? PA_MFMA_NBUF_FP8 : PA_MFMA_NBUF;
   static_assert(BS % 16 == 0 && D % 64 == 0, "shape");
   using M = Mma<QT>;
   // PV operand type: f16 for fp8 caches (decoded e4m3fn is exact in f16,
@@ -82,6 +89,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   __shared__ int s_hist[PART ? 1 : WAVES * kSchedKeys];
   __shared__ float s_state[WAVES > 1 ? (WAVES - 1) * kWave * NSTATE : 1];
   __shared__ __attribute__((aligned(16))) float s_new[PART ? 4 : 2 * D];   // fused append
+  __shared__ uint16_t s_new_bits[PART ? 2 : 2 * D];
   __shared__ int s_table[table_lds_ints(WAVES)];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int lane = threadIdx.x & 63;
@@ -170,7 +178,8 @@ void decode_mfma_kernel(const DecodeParams p) {
   if (bad_len || (PART && L <= 0)) {
     if (take_new) {
       nt.load(p, s, kvh, lane);
-      nt.template store<QT, CT, BS>(p, slot, kvh, lane, s_new);
+      nt.template stage<QT, CT>(p, lane, s_new, s_new_bits);
+      NewToken<D>::template write<CT, BS>(p, slot, kvh, lane, s_new_bits);
     }
     if (bad_len && wave == 0) {
       float4_t o[NPV];
@@ -347,14 +356,16 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
   };
 
+  // the new token's loads go first, then the prologue's tile loads
+  if (take_new) nt.load(p, s, kvh, lane);
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u) issue(kb[u], vb[u], u);
 
   if (take_new) {
-    // store the token; its cached values land in s_new.  Logit: lane group
-    // g's q dims (qb) against the same dims of the stored K row
-    nt.load(p, s, kvh, lane);
-    nt.template store<QT, CT, BS>(p, slot, kvh, lane, s_new);
+    // the token's cached values land in s_new (its store into the cache
+    // comes after the stream).  Logit: lane group g's q dims (qb) against
+    // the same dims of the cached K row
+    nt.template stage<QT, CT>(p, lane, s_new, s_new_bits);
     __builtin_amdgcn_wave_barrier();
     float xn = 0.0f;
 #pragma unroll
@@ -401,6 +412,9 @@ void decode_mfma_kernel(const DecodeParams p) {
       if (t < ntiles) process(kb[u], vb[u], (my_first + t == last_tile) && (last_len < BS));
     }
   }
+
+  // the new token into its slot, after the stream
+  if (take_new) NewToken<D>::template write<CT, BS>(p, slot, kvh, lane, s_new_bits);
 
   bool bad = table_bad(tw);
   if constexpr (WAVES > 1) {

@@ -174,6 +174,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   __shared__ int s_hist[PART ? 1 : WAVES * kSchedKeys];
   __shared__ float s_state[WAVES > 1 ? (WAVES - 1) * kWave * NSTATE : 1];
   __shared__ __attribute__((aligned(16))) float s_new[PART ? 4 : 2 * D];   // fused append
+  __shared__ uint16_t s_new_bits[PART ? 2 : 2 * D];
   __shared__ int s_table[table_lds_ints(WAVES)];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
@@ -252,7 +253,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   if (bad_len || (PART && L <= 0)) {
     if (take_new) {
       nt.load(p, s, kvh, lane);
-      nt.template store<QT, CT, BS>(p, slot, kvh, lane, s_new);
+      nt.template stage<QT, CT>(p, lane, s_new, s_new_bits);
+      NewToken<D>::template write<CT, BS>(p, slot, kvh, lane, s_new_bits);
     }
     if (bad_len && wave == 0) {
       float nanv[E];
@@ -357,16 +359,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
     __builtin_amdgcn_wave_barrier();
   };
 
-  // prologue: NBUF - 1 tiles in flight
+  // the new token's loads go first, then the prologue: NBUF - 1 tiles in
+  // flight
+  if (take_new) nt.load(p, s, kvh, lane);
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u) issue(kb[u], vb[u], u);
 
   if (take_new) {
-    // store the token (slot -1: another head of the group stores it); its
-    // cached values land in s_new.  Logit: the lane's q chunk against the
-    // same dims of the stored K row, summed over the LPT lanes of a row
-    nt.load(p, s, kvh, lane);
-    nt.template store<QT, CT, BS>(p, slot, kvh, lane, s_new);
+    // the token's cached values land in s_new (its store into the cache
+    // comes after the stream).  Logit: the lane's q chunk against the same
+    // dims of the cached K row, summed over the LPT lanes of a row
+    nt.template stage<QT, CT>(p, lane, s_new, s_new_bits);
     __builtin_amdgcn_wave_barrier();
     const float* kk = s_new + (lane % LPT) * VEC;
     float xp = 0.0f;
@@ -407,6 +410,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
       }
     }
   }
+
+  // the new token into its slot (slot -1: another head of the group stores
+  // it), after the stream
+  if (take_new) NewToken<D>::template write<CT, BS>(p, slot, kvh, lane, s_new_bits);
 
   // lanes sharing head dims add up (one reference max); the weight sum adds
   // one lane per K token row

@@ -251,7 +251,13 @@ __device__ __forceinline__ const uint16_t* new_token_row(const DecodeParams& p, 
 }
 
 // The new token of sequence s, kv head kvh, spread over one wavefront: lane
-// l holds dims l, l + 64, ... of its K and V input rows.
+// l holds dims l, l + 64, ... of its K and V input rows.  Used in three
+// steps: load (issued before the wavefront's first tile loads, so waiting
+// for it does not wait for them), stage (the values the cache will hold, into
+// LDS, from registers), write (the stores into the cache slot, issued after
+// the wavefront's tile stream: vector loads and stores share one in-order
+// counter on this target, so an early store would hold back the waits for
+// every tile loaded after it).
 template <int D>
 struct NewToken {
   static constexpr int N = D / kWave;
@@ -268,16 +274,42 @@ struct NewToken {
     }
   }
 
+  // The values the cache holds for the token (code units, fp32) into LDS,
+  // s_kv[d] for K and s_kv[D + d] for V, and what write() stores (the input
+  // bits, or the fp8 codes) into s_bits[d] / s_bits[D + d], so that no
+  // register holds the token through the stream.
+  template <typename IT, typename CT>
+  __device__ __forceinline__ void stage(const DecodeParams& p, int lane, float* s_kv,
+                                        uint16_t* s_bits) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int d = lane + kWave * i;
+      if constexpr (CT::kBytes == 2) {
+        s_kv[d] = in_value<IT>(k[i]);
+        s_kv[D + d] = in_value<IT>(v[i]);
+        s_bits[d] = k[i];
+        s_bits[D + d] = v[i];
+      } else {
+        const uint32_t kq = e4m3fn_encode(in_value<IT>(k[i]) * p.k_inv_scale);
+        const uint32_t vq = e4m3fn_encode(in_value<IT>(v[i]) * p.v_inv_scale);
+        s_kv[d] = fp8x2_to_f32<false>(kq)[0];
+        s_kv[D + d] = fp8x2_to_f32<false>(vq)[0];
+        s_bits[d] = (uint16_t)kq;
+        s_bits[D + d] = (uint16_t)vq;
+      }
+    }
+  }
+
   // Store the token at its slot (K row of the token-major tile; V dims at
   // (t/4*D + d)*4 + t%4 of the quad tile) exactly as the cache write does,
-  // and put the values the cache now holds (code units, fp32) into LDS:
-  // s_kv[d] for K, s_kv[D + d] for V.
-  template <typename IT, typename CT, int BS>
-  __device__ __forceinline__ void store(const DecodeParams& p, int32_t slot, int kvh, int lane,
-                                        float* s_kv) const {
+  // from what stage() left in s_bits; a negative slot or one past the pool
+  // stores nothing.
+  template <typename CT, int BS>
+  static __device__ __forceinline__ void write(const DecodeParams& p, int32_t slot, int kvh,
+                                               int lane, const uint16_t* s_bits) {
     const int64_t blk = slot / BS;
     const int off = slot % BS;
-    const bool write = slot >= 0 && blk < p.num_blocks;
+    if (slot < 0 || blk >= p.num_blocks) return;
     const int64_t tile = (blk * p.num_kv_heads + kvh) * (int64_t)(BS * D);   // elements
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -285,21 +317,11 @@ struct NewToken {
       const int64_t ko = tile + (int64_t)off * D + d;
       const int64_t vo = tile + ((int64_t)(off >> 2) * D + d) * 4 + (off & 3);
       if constexpr (CT::kBytes == 2) {
-        if (write) {
-          reinterpret_cast<uint16_t*>(const_cast<void*>(p.k_cache))[ko] = k[i];
-          reinterpret_cast<uint16_t*>(const_cast<void*>(p.v_cache))[vo] = v[i];
-        }
-        s_kv[d] = in_value<IT>(k[i]);
-        s_kv[D + d] = in_value<IT>(v[i]);
+        reinterpret_cast<uint16_t*>(const_cast<void*>(p.k_cache))[ko] = s_bits[d];
+        reinterpret_cast<uint16_t*>(const_cast<void*>(p.v_cache))[vo] = s_bits[D + d];
       } else {
-        const uint32_t kc = e4m3fn_encode(in_value<IT>(k[i]) * p.k_inv_scale);
-        const uint32_t vc = e4m3fn_encode(in_value<IT>(v[i]) * p.v_inv_scale);
-        if (write) {
-          reinterpret_cast<uint8_t*>(const_cast<void*>(p.k_cache))[ko] = (uint8_t)kc;
-          reinterpret_cast<uint8_t*>(const_cast<void*>(p.v_cache))[vo] = (uint8_t)vc;
-        }
-        s_kv[d] = fp8x2_to_f32<false>(kc)[0];
-        s_kv[D + d] = fp8x2_to_f32<false>(vc)[0];
+        reinterpret_cast<uint8_t*>(const_cast<void*>(p.k_cache))[ko] = (uint8_t)s_bits[d];
+        reinterpret_cast<uint8_t*>(const_cast<void*>(p.v_cache))[vo] = (uint8_t)s_bits[D + d];
       }
     }
   }

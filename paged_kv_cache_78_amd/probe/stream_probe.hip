@@ -1,6 +1,7 @@
-// HBM read-rate probe with the decode kernels' tile stream: random 4 KiB
-// tiles, 16-byte lane loads (one contiguous KiB per load instruction), a
-// ring of three tiles in flight per wavefront, optional non-temporal policy.
+// HBM read-rate probe with the decode kernels' tile stream: random tiles of
+// 4 KiB (a 16-bit K or V tile at block size 16, head size 128) or 2 KiB (the
+// same in fp8), 16-byte lane loads (one contiguous KiB per load instruction),
+// a ring of 2-8 tiles in flight per wavefront, optional non-temporal policy.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -10,9 +11,6 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
-constexpr int kTileBytes = 4096;
-constexpr int kLoads = kTileBytes / 1024;
-constexpr int kRing = 3;
 constexpr int kWaves = 4;
 
 template <int POLICY>
@@ -20,12 +18,13 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY));
 }
 
-template <int POLICY>
+template <int POLICY, int kTileBytes, int kRing>
 __global__ __launch_bounds__(64 * kWaves) void stream_probe_kernel(
     const char* pool, int64_t num_tiles, const int32_t* tile_ids, int num_waves,
     int tiles_per_wave, uint32_t* sink) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
   const int lane = threadIdx.x & 63;
+  constexpr int kLoads = kTileBytes / 1024;
   if (wave >= num_waves) return;
   // the wavefront's tile ids, 64 per VGPR (one per lane), read with
   // v_readlane as the decode kernels read their block tables; loads past the
@@ -73,22 +72,53 @@ __global__ __launch_bounds__(64 * kWaves) void stream_probe_kernel(
   sink[(int64_t)wave * 64 + lane] = x;
 }
 
+
+template <int POLICY, int TB>
+hipError_t launch_ring(int ring, dim3 grid, hipStream_t st, const char* pool, int64_t num_tiles,
+                       const int32_t* ids, int num_waves, int tpw, uint32_t* sink) {
+  switch (ring) {
+#define PA_PROBE_RING(R)                                                                       \
+  case R:                                                                                      \
+    hipLaunchKernelGGL((stream_probe_kernel<POLICY, TB, R>), grid, dim3(64 * kWaves), 0, st,   \
+                       pool, num_tiles, ids, num_waves, tpw, sink);                            \
+    break;
+    PA_PROBE_RING(2)
+    PA_PROBE_RING(3)
+    PA_PROBE_RING(4)
+    PA_PROBE_RING(6)
+    PA_PROBE_RING(8)
+#undef PA_PROBE_RING
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" int pa_probe_stream(const void* pool, int64_t num_tiles, const int32_t* tile_ids,
-                               int32_t num_waves, int32_t tiles_per_wave, int32_t nontemporal,
-                               uint32_t* sink, void* stream) {
+                               int32_t num_waves, int32_t tiles_per_wave, int32_t tile_bytes,
+                               int32_t in_flight, int32_t nontemporal, uint32_t* sink,
+                               void* stream) {
   if (!pool || !tile_ids || !sink || num_tiles <= 0 || num_waves <= 0 || tiles_per_wave <= 0 ||
       tiles_per_wave > (1 << 24))
     return -2;
+  if ((tile_bytes != 2048 && tile_bytes != 4096) ||
+      (in_flight != 2 && in_flight != 3 && in_flight != 4 && in_flight != 6 && in_flight != 8))
+    return -2;
   const dim3 grid((num_waves + kWaves - 1) / kWaves);
+  const char* pl = static_cast<const char*>(pool);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
   if (nontemporal)
-    hipLaunchKernelGGL(stream_probe_kernel<2>, grid, dim3(64 * kWaves), 0, (hipStream_t)stream,
-                       static_cast<const char*>(pool), num_tiles, tile_ids, num_waves,
-                       tiles_per_wave, sink);
+    e = tile_bytes == 2048
+            ? launch_ring<2, 2048>(in_flight, grid, st, pl, num_tiles, tile_ids, num_waves,
+                                   tiles_per_wave, sink)
+            : launch_ring<2, 4096>(in_flight, grid, st, pl, num_tiles, tile_ids, num_waves,
+                                   tiles_per_wave, sink);
   else
-    hipLaunchKernelGGL(stream_probe_kernel<0>, grid, dim3(64 * kWaves), 0, (hipStream_t)stream,
-                       static_cast<const char*>(pool), num_tiles, tile_ids, num_waves,
-                       tiles_per_wave, sink);
-  return hipGetLastError() == hipSuccess ? 0 : -6;
+    e = tile_bytes == 2048
+            ? launch_ring<0, 2048>(in_flight, grid, st, pl, num_tiles, tile_ids, num_waves,
+                                   tiles_per_wave, sink)
+            : launch_ring<0, 4096>(in_flight, grid, st, pl, num_tiles, tile_ids, num_waves,
+                                   tiles_per_wave, sink);
+  return e == hipSuccess ? 0 : -6;
 }
