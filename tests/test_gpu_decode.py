@@ -260,14 +260,11 @@ def _run_slots(BS):
     return [x for r in runs for x in r]
 
 
-@pytest.mark.parametrize("cache_fmt,D,BS", [("f16", 128, 16), ("bf16", 64, 32),
-                                            ("e4m3fn", 128, 16), ("e4m3fn", 64, 32)])
-def test_cache_write_runs_bit_exact(cache_fmt, D, BS):
-    """Whole token quads are written four tokens at a time, the rest token by
-    token: both against the oracle's write, bit for bit."""
-    gen = torch.Generator().manual_seed(11)
-    KVH, NB = 3, 9
-    slots = torch.tensor(_run_slots(BS), dtype=torch.int32)
+def _write_and_compare(slots, cache_fmt, D, BS, KVH, NB, seed):
+    """pa_cache_write of random K/V into a random pool against the oracle's
+    write, both caches compared bit for bit."""
+    gen = torch.Generator().manual_seed(seed)
+    slots = torch.tensor(slots, dtype=torch.int32)
     T = slots.numel()
     in_dt = torch.bfloat16 if cache_fmt == "bf16" else torch.float16
     k = torch.randn((T, KVH, D), generator=gen).to(in_dt)
@@ -290,6 +287,52 @@ def test_cache_write_runs_bit_exact(cache_fmt, D, BS):
                                 to_numpy_bits(vc), slots.numpy(), BS, cache_fmt, ks, vs)
     assert to_numpy_bits(gk).tobytes() == ok.tobytes()
     assert to_numpy_bits(gv).tobytes() == ov.tobytes()
+
+
+@pytest.mark.parametrize("cache_fmt,D,BS", [("f16", 128, 16), ("bf16", 64, 32),
+                                            ("e4m3fn", 128, 16), ("e4m3fn", 64, 32)])
+def test_cache_write_runs_bit_exact(cache_fmt, D, BS):
+    """Whole token quads are written four tokens at a time, the rest token by
+    token: both against the oracle's write, bit for bit."""
+    _write_and_compare(_run_slots(BS), cache_fmt, D, BS, KVH=3, NB=9, seed=11)
+
+
+def _ragged_chunk_slots(rng, BS, NB, min_tokens):
+    """Prefill-like slots over a permuted pool: sequences with a cached prefix
+    of any length (chunks start mid-quad and mid-block) and a chunk of 1..90
+    tokens, about 1% of tokens skipped (-1), one quad in reversed order, and
+    a token count that is not a multiple of 8."""
+    perm = rng.permutation(NB).tolist()
+    slots = []
+    while len(slots) < min_tokens:
+        ctx, n = int(rng.integers(0, 40)), int(rng.integers(1, 91))
+        nblk = -(-(ctx + n) // BS)
+        blocks, perm = perm[:nblk], perm[nblk:]
+        assert len(blocks) == nblk, "pool too small"
+        slots += [blocks[t // BS] * BS + t % BS for t in range(ctx, ctx + n)]
+    slots = np.array(slots, dtype=np.int64)
+    slots[rng.random(slots.size) < 0.01] = -1
+    q = 4 * int(rng.integers(10, slots.size // 4 - 10))
+    slots[q:q + 4] = slots[q:q + 4][::-1].copy()
+    if slots.size % 8 == 0:
+        slots = slots[:-3]
+    return slots.tolist()
+
+
+@pytest.mark.parametrize("cache_fmt,D,BS", [("f16", 128, 16), ("bf16", 64, 32),
+                                            ("e4m3fn", 128, 16)])
+def test_cache_write_wide_grid_ragged_bit_exact(cache_fmt, D, BS):
+    """A write of 1,100+ tokens over 32 kv heads, enough wavefronts that each
+    takes several token quads: groups whose quads are all whole and aligned
+    take the load-all-then-store path, the others (a chunk's first or last
+    tokens, skips, the reversed quad, the ragged end) the per-token one; both
+    against the oracle's write, bit for bit."""
+    rng = np.random.default_rng(31)
+    KVH, NB = 32, 160 if BS == 16 else 100
+    slots = _ragged_chunk_slots(rng, BS, NB, min_tokens=1100)
+    T = len(slots)
+    assert T % 8 != 0 and -(-T // 8) * KVH >= 4096
+    _write_and_compare(slots, cache_fmt, D, BS, KVH=KVH, NB=NB, seed=12)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
