@@ -36,6 +36,7 @@ struct Mma<F16> {
     const half2_t v = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, v);
   }
+  static constexpr uint32_t kOne2 = 0x3C003C00u;   // packed pair of 1.0
   // acc + the two 16-bit values of w (exact products, one fp32 sum)
   static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
     const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
@@ -67,6 +68,7 @@ struct Mma<BF16> {
     return __builtin_bit_cast(uint32_t, r);
   }
   static __device__ __forceinline__ uint32_t pack_pk(float lo, float hi) { return pack(lo, hi); }
+  static constexpr uint32_t kOne2 = 0x3F803F80u;   // packed pair of 1.0
   static __device__ __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
   static __device__ __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
   static __device__ __forceinline__ float sum2(uint32_t w, float acc) {

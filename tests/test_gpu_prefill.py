@@ -75,6 +75,20 @@ def test_chunks_against_oracle(dtype, H, KVH, D, BS):
     _check(b, f"{dtype} H{H} KVH{KVH} D{D} BS{BS}")
 
 
+@pytest.mark.parametrize("dtype,cache,H,KVH,D,BS", [
+    ("f16", "", 8, 2, 64, 32), ("bf16", "", 4, 4, 128, 16), ("bf16", "e4m3fn", 4, 2, 128, 32),
+])
+def test_long_contexts_cross_table_windows(dtype, cache, H, KVH, D, BS):
+    """Contexts of up to 4,300 keys: the block-table entries of later key
+    stages come from the second and later windows of 64 entries (past 1,024
+    keys at block size 16, past 2,048 at 32), and the context ends inside a
+    stage at several offsets."""
+    q_lens = [40, 7, 130, 1]
+    ctx = [2300, 4200, 1100, 3333]
+    b = workloads.prefill_batch(38, q_lens, ctx, H, KVH, D, BS, dtype, cache)
+    _check(workloads.poison_prefill(b), f"long {dtype}/{cache or dtype} H{H} KVH{KVH} D{D} BS{BS}")
+
+
 def test_many_sequences():
     """More than 64 sequences (the workgroup queue then runs item by item
     instead of by decreasing context), with equal contexts among them."""
