@@ -11,17 +11,19 @@
 //
 // A physical block is KVH contiguous (block, kv head) tiles, so one block of
 // K (and one of V) is a single contiguous run of block_bytes.  Workgroup
-// (chunk, pair, tensor) moves kChunk bytes of it with 16-byte loads and
-// stores, kUnroll loads in flight per thread before the first store (host
-// memory behind the link has a long latency).
+// (chunk, pair, tensor) is one wavefront moving kChunk = 1 KiB of it, one
+// 16-byte load and store per lane: many small workgroups keep more of the
+// copy in flight across the chip than fewer ones with several loads each
+// (on 2048 Llama-7B blocks, 5.9 TB/s of read + write against 4.9 TB/s for
+// 16 KiB workgroups with four loads per lane, and 5.4 TB/s for a plain
+// device copy of the same size).
 #include "pa_kernels.h"
 
 namespace pa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
-constexpr int64_t kChunk = (int64_t)kThreads * 16 * kUnroll;   // 16 KiB
+constexpr int kThreads = 64;
+constexpr int64_t kChunk = (int64_t)kThreads * 16;   // 1 KiB
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
@@ -30,22 +32,13 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const BlockCopyPa
   const int32_t src = p.mapping[2 * pair];
   const int32_t dst = p.mapping[2 * pair + 1];
   if (src < 0 || dst < 0 || src >= p.src_num_blocks || dst >= p.dst_num_blocks) return;
+  const int64_t off = (int64_t)blockIdx.x * kChunk + (int64_t)threadIdx.x * 16;
+  if (off >= p.block_bytes) return;
   const char* from = reinterpret_cast<const char*>(blockIdx.z == 0 ? p.src_k : p.src_v) +
                      (int64_t)src * p.block_bytes;
   char* to = reinterpret_cast<char*>(blockIdx.z == 0 ? p.dst_k : p.dst_v) +
              (int64_t)dst * p.block_bytes;
-  const int64_t base = (int64_t)blockIdx.x * kChunk + (int64_t)threadIdx.x * 16;
-  u32x4 w[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t off = base + (int64_t)u * kThreads * 16;
-    if (off < p.block_bytes) w[u] = *reinterpret_cast<const u32x4*>(from + off);
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t off = base + (int64_t)u * kThreads * 16;
-    if (off < p.block_bytes) *reinterpret_cast<u32x4*>(to + off) = w[u];
-  }
+  *reinterpret_cast<u32x4*>(to + off) = *reinterpret_cast<const u32x4*>(from + off);
 }
 
 }  // namespace
