@@ -72,7 +72,9 @@ void decode_mfma_kernel(const DecodeParams p) {
   constexpr int E = 16 / (4 * ESZ);         // head dims per 16-byte V load (4 tokens each)
   constexpr int NVL = NPV / E;              // 16-byte V loads per sub-tile
   constexpr int NKL = ESZ == 2 ? NQK : NQK / 2;   // 16-byte K loads per sub-tile
-  constexpr int NBUF = ESZ == 1 ? PA_MFMA_NBUF_FP8 : PA_MFMA_NBUF;
+  // fp8 tiles in flight: three of 16 tokens, two of 32 (64 tokens, and no
+  // spills under the fp8 occupancy's register budget)
+  constexpr int NBUF = ESZ == 1 ? (BS == 32 ? 2 : PA_MFMA_NBUF_FP8) : PA_MFMA_NBUF;
   static_assert(BS % 16 == 0 && D % 64 == 0, "shape");
   using M = Mma<QT>;
   // PV operand type: f16 for fp8 caches (decoded e4m3fn is exact in f16,
