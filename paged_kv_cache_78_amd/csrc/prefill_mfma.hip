@@ -11,7 +11,7 @@
 //
 // Layout of the work: the n_s * G query rows of (sequence, kv head) (G query
 // heads per kv head, row r = token r / G, head r % G) are cut into workgroup
-// chunks of ROWS = 4 wavefronts x R blocks of 16 rows.  A workgroup walks the
+// units of ROWS = 4 wavefronts x R blocks of 16 rows.  A workgroup walks the
 // keys in stages of 32 (two 16-key sub-tiles): its 256 threads copy the
 // stage's K and V tiles (gathered through the block table) into LDS once, and
 // every wavefront multiplies them with its R row blocks:
@@ -31,10 +31,13 @@
 // hit every bank once.  The copies go from global memory straight into LDS
 // (global_load_lds), three stages in a ring.
 //
-// Work mapping: workgroups go to the XCDs round robin, so the chunks of one
-// (sequence, kv head) are given workgroup indices that land on the same XCD
-// and share its L2, one after the other, the chunk with more keys first;
-// the sequences' items are taken by decreasing context.
+// Work mapping: each XCD has a queue of work units (the chunks of its
+// (sequence, kv head) items, one after the other, the chunk with more keys
+// first, items by decreasing context), so the chunks of an item share that
+// XCD's L2.  The workgroups are persistent, as many as are resident at once:
+// workgroup b runs on XCD b % 8 (they go to the XCDs round robin) and walks
+// that XCD's queue in rounds, without a new dispatch per unit.  The sum of a
+// row's weights comes from the matrix core (an all-ones A operand).
 //
 // Weight precision, fp8 decoding and masking follow the decode kernels: P in
 // f16 (f16 and fp8 caches) or split into two bf16 parts (bf16 caches); keys
