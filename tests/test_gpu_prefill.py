@@ -170,3 +170,14 @@ def test_negative_and_zero_scale(scale, dtype):
     b = workloads.prefill_batch(38, [9, 40, 1], [20, 0, 70], 8, 2, 128, 16, dtype)
     b = workloads.synth.replace(workloads.poison_prefill(b), scale=scale)
     _check(b, f"scale {scale} {dtype}")
+
+
+@pytest.mark.parametrize("scale", [0.7, -2.0, 4.0])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_large_scales(scale, dtype):
+    """Scales far above 1/sqrt(D), positive and negative: large logits and
+    sharply peaked weights, where any rounding of the logits before the
+    exponential would show."""
+    b = workloads.prefill_batch(39, [9, 40, 1, 17], [20, 0, 70, 33], 8, 2, 128, 16, dtype)
+    b = workloads.synth.replace(workloads.poison_prefill(b), scale=scale)
+    _check(b, f"scale {scale} {dtype}")
