@@ -29,7 +29,11 @@
 // The 16-byte granules of each K row in LDS are XOR-permuted by the key and
 // V's token-quad regions are padded by 128 bytes, so that the operand reads
 // hit every bank once.  The copies go from global memory straight into LDS
-// (global_load_lds), three stages in a ring.
+// (global_load_lds), three stages in a ring.  Three workgroups share a CU
+// (three wavefronts per SIMD: at most 168 registers each, and 3 x 52.75 KB of
+// LDS at head size 128): a wavefront alone keeps its SIMD busy little more
+// than half the time (the K/V reads from LDS, the product chains and the
+// barrier each stall it), and the other two fill much of the rest.
 //
 // Work mapping: each XCD has a queue of work units (the chunks of its
 // (sequence, kv head) items, one after the other, the chunk with more keys
@@ -111,11 +115,11 @@ __device__ __forceinline__ float max8(const float (&v)[8]) {
 }
 
 template <typename QT, typename CT, int D, int BS, bool CAUSAL, int R>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(const PrefillParams p,
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3))) void prefill_mfma_kernel(const PrefillParams p,
                                                                    int chunks, int units_x) {
   using Sh = PfShape<QT, CT, D, BS, R>;
   constexpr int ESZ = Sh::ESZ, NQK = Sh::NQK, NPV = Sh::NPV;
-  constexpr int ROWB = Sh::ROWB, GPR = Sh::GPR, KB = Sh::KB, NREG = Sh::NREG, KPR = Sh::KPR;
+  constexpr int ROWB = Sh::ROWB, GPR = Sh::GPR, KB = Sh::KB, KPR = Sh::KPR;
   constexpr int QB = Sh::QB, QPR = Sh::QPR, VREG = Sh::VREG, STAGE = Sh::STAGE;
   constexpr int NREGW = Sh::NREGW, ROWS = Sh::ROWS, TILE_BYTES = Sh::TILE_BYTES;
   constexpr int BPS = kPfKeys / BS;   // blocks per stage
@@ -382,18 +386,26 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const float sl = fmaxf(fabsf(p.qk_scale_log2), __FLT_MIN__);
 
     // running maximum starts finite, so that exp2(logit - m) needs no guard:
-    // a masked logit (-inf) gives 0 whatever m is.  The sum of the weights
-    // comes from the matrix core as well: one more product per row block, of
-    // an all-ones A operand with the packed weights, leaves in every lane of
-    // column n the sum of row n's weights as they enter the PV product.
+    // a masked logit (-inf) gives 0 whatever m is.  The sum of the weights,
+    // as they enter the PV product, comes with 16-bit caches from the matrix
+    // core: one more product per row block, of an all-ones A operand with the
+    // packed weights, leaves in every lane of column n the sum of row n's
+    // weights (lacc).  With fp8 caches, whose operand decoding needs more
+    // registers, each lane sums its own 8 weights per stage with v_dot2
+    // (exact products with 1, an fp32 sum: lsum), and the 4 lanes of a row add
+    // theirs at the end; the 12 registers of lacc would otherwise spill at
+    // three wavefronts per SIMD.
+    constexpr bool kSumValu = ESZ == 1;
     float m[R];
     float4_t lacc[R];
+    float lsum[R];
     float4_t acc[R][NPV];
     const u32x4_t ones = u32x4_t{MV::kOne2, MV::kOne2, MV::kOne2, MV::kOne2};
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       m[r] = -__FLT_MAX__;
       lacc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
+      lsum[r] = 0.0f;
 #pragma unroll
       for (int jj = 0; jj < NPV; ++jj) acc[r][jj] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -437,7 +449,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     // the wavefront stops inside the stage, its logits past the row limit are
     // -inf; unmasked: every key counts for every valid row and the logits go
     // straight from the products to exp2), then the accumulators meet a single
-    // product path, so each product updates them in place.
+    // product path, so each product updates them in place.  The weights of
+    // both row blocks are taken first, then each V operand is read from LDS
+    // just before its two products: a wavefront holds one or two V operands
+    // instead of all NPV, which fits the kernel in the registers of three
+    // wavefronts per SIMD (the latency a wavefront leaves exposed is covered
+    // by the other two).
     auto compute = [&](bool masked, int t, int boff) {
       const char* kb = &s_kv[0][0] + boff;
       const char* vb = kb + KB;
@@ -455,10 +472,6 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
           for (int r = 0; r < R; ++r) sc[r][u] = M::qk(ka, qb[r][cc], sc[r][u]);
         }
       }
-      // the V operands, read while the weights are computed
-      u32x4_t va[NPV];
-#pragma unroll
-      for (int jj = 0; jj < NPV; ++jj) va[jj] = v_operand(vb, jj);
       // Masked stage (some row of the wavefront stops inside it): products of
       // keys past a row's limit become -inf, so their logits (times sl > 0)
       // are -inf and their weights 0.  Then the row maxima of the stage.
@@ -486,8 +499,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
       // maximum passes it by more than the slack (weights stay below 2^slack);
       // then the accumulators are rescaled.  Decided before any weight is
       // taken, so that the weights, their packing and the products that use
-      // them form one block: the products of one row block overlap the
-      // exponentials of the next.
+      // them form one block.
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -498,12 +510,15 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
           const float alpha = exp2_hw(m[r] - mn);
           m[r] = mn;
           lacc[r] *= alpha;
+          lsum[r] *= alpha;
 #pragma unroll
           for (int jj = 0; jj < NPV; ++jj) acc[r][jj] *= alpha;
         }
       }
       // per row block: the weights exp2(logit - m), packed as the PV B
-      // operand, then the products and the weights' sum
+      // operand (bf16 caches: and the remainder of each weight, packed again),
+      // and the weights' sum
+      u32x4_t pb[R], pl[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         float pr[8];
@@ -513,39 +528,32 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         uint32_t w[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) w[k] = MV::pack_pk(pr[2 * k], pr[2 * k + 1]);
-        const u32x4_t pb = u32x4_t{w[0], w[1], w[2], w[3]};
-        u32x4_t pl = u32x4_t{0u, 0u, 0u, 0u};
+        pb[r] = u32x4_t{w[0], w[1], w[2], w[3]};
+        pl[r] = u32x4_t{0u, 0u, 0u, 0u};
         if constexpr (kSplitP) {
           uint32_t v2[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k)
             v2[k] = MV::pack_pk(pr[2 * k] - MV::lo(w[k]), pr[2 * k + 1] - MV::hi(w[k]));
-          pl = u32x4_t{v2[0], v2[1], v2[2], v2[3]};
+          pl[r] = u32x4_t{v2[0], v2[1], v2[2], v2[3]};
         }
+        if constexpr (kSumValu) {
 #pragma unroll
-        for (int jj = 0; jj < NPV; ++jj) {
-          acc[r][jj] = MV::qk(va[jj], pb, acc[r][jj]);
-          if constexpr (kSplitP) acc[r][jj] = MV::qk(va[jj], pl, acc[r][jj]);
+          for (int k = 0; k < 4; ++k) lsum[r] = MV::sum2(w[k], lsum[r]);
+        } else {
+          lacc[r] = MV::qk(ones, pb[r], lacc[r]);
+          if constexpr (kSplitP) lacc[r] = MV::qk(ones, pl[r], lacc[r]);
         }
-        lacc[r] = MV::qk(ones, pb, lacc[r]);
-        if constexpr (kSplitP) lacc[r] = MV::qk(ones, pl, lacc[r]);
       }
-      if constexpr (R == 2 && !kSplitP) {
-        // Order of the block above: the first row block's weights (8 fma, 8
-        // exp, 4 packs), then its NPV + 1 products each followed by up to 3 of
-        // the second row block's weight instructions, then the second row
-        // block's products.
-        // Instruction classes of the scheduling groups: vector ALU including
-        // the transcendental unit (0x002 | 0x400), matrix core (0x008).
-        constexpr int kGroupValu = 0x002 | 0x400;
-        constexpr int kGroupMfma = 0x008;
-        __builtin_amdgcn_sched_group_barrier(kGroupValu, 20, 0);
+      // the PV products, V operand by V operand
 #pragma unroll
-        for (int k = 0; k < NPV + 1; ++k) {
-          __builtin_amdgcn_sched_group_barrier(kGroupMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kGroupValu, 3, 0);
+      for (int jj = 0; jj < NPV; ++jj) {
+        const u32x4_t va = v_operand(vb, jj);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          acc[r][jj] = MV::qk(va, pb[r], acc[r][jj]);
+          if constexpr (kSplitP) acc[r][jj] = MV::qk(va, pl[r], acc[r][jj]);
         }
-        __builtin_amdgcn_sched_group_barrier(kGroupMfma, NPV + 1, 0);
       }
     };
 
@@ -677,7 +685,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     float4_t o[R][NPV];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float lt = lacc[r][0];
+      float lt = lacc[r][0];
+      if constexpr (kSumValu) {
+        lt = lsum[r];
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+      }
       const float inv = bad_any ? __builtin_nanf("") : (lt > 0.0f ? p.v_scale / lt : 0.0f);
 #pragma unroll
       for (int jj = 0; jj < NPV; ++jj) o[r][jj] = acc[r][jj] * inv;
