@@ -105,6 +105,21 @@ def test_fp8_cache(H, KVH, D, BS):
     _check(workloads.poison_prefill(b), f"fp8 H{H} KVH{KVH} D{D} BS{BS}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("BS", [16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype,cache", [("f16", ""), ("bf16", ""), ("f16", "e4m3fn"),
+                                         ("bf16", "e4m3fn")])
+def test_every_kernel_instantiation(dtype, cache, D, BS, causal):
+    """One small batch per compiled kernel (query type, cache type, head
+    size, block size, causal or not): grouped heads, a chunk longer than one
+    128-row unit, an empty cached prefix and a context ending inside a
+    stage."""
+    b = workloads.prefill_batch(40, [5, 140, 1], [70, 0, 33], 8, 2, D, BS, dtype, cache)
+    _check(workloads.poison_prefill(b), f"{dtype}/{cache or dtype} D{D} BS{BS} causal={causal}",
+           causal=causal)
+
+
 def test_non_causal():
     b = workloads.prefill_batch(33, [7, 20], [13, 44], 8, 2, 128, 16, "f16")
     _check(workloads.poison_prefill(b), "non-causal", causal=False)
