@@ -120,6 +120,18 @@ def test_every_kernel_instantiation(dtype, cache, D, BS, causal):
            causal=causal)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype,H,KVH,D", [("f16", 32, 2, 128), ("bf16", 16, 1, 64),
+                                           ("f16", 2, 2, 128)])
+def test_group_sizes_at_the_limits(dtype, H, KVH, D, causal):
+    """16 query heads per kv head (the largest group the API takes) and one:
+    with 16 heads a 128-row unit covers 8 query tokens, so chunks of 150
+    tokens span 19 units of one item; with one head it covers 128 tokens."""
+    b = workloads.prefill_batch(41, [150, 9, 1], [40, 300, 0], H, KVH, D, 16, dtype)
+    _check(workloads.poison_prefill(b), f"{dtype} H{H} KVH{KVH} D{D} causal={causal}",
+           causal=causal)
+
+
 def test_non_causal():
     b = workloads.prefill_batch(33, [7, 20], [13, 44], 8, 2, 128, 16, "f16")
     _check(workloads.poison_prefill(b), "non-causal", causal=False)
