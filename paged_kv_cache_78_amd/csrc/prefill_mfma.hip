@@ -393,8 +393,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
     // weights (lacc).  With fp8 caches, whose operand decoding needs more
     // registers, each lane sums its own 8 weights per stage with v_dot2
     // (exact products with 1, an fp32 sum: lsum), and the 4 lanes of a row add
-    // theirs at the end; the 12 registers of lacc would otherwise spill at
-    // three wavefronts per SIMD.
+    // theirs at the end; lacc and its all-ones operand (12 registers) would
+    // otherwise spill at three wavefronts per SIMD.
     constexpr bool kSumValu = ESZ == 1;
     float m[R];
     float4_t lacc[R];
