@@ -1,7 +1,7 @@
 """Benchmark of one decode step of paged attention on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1] [--unfused]
-    python bench.py --op stream | prefill | copy_blocks | swap_out | swap_in | fragmentation
+    python bench.py --op stream | prefill | prefill_long | copy_blocks | swap_out | swap_in | fragmentation
 
 A step is one pass of the hot path over one synthetic batch that is already
 resident in HBM: every sequence's new token is stored in its cache slot and
@@ -335,26 +335,28 @@ def bench_fragmentation(args, pa):
 PEAK_MFMA_F16_TFLOPS = 2500.0
 
 
-def prefill_flops(b) -> int:
-    """QK and PV multiply-adds of every (query, key) pair a causal chunk
-    attends: 4 * D flops per pair per query head."""
+def prefill_flops(b, causal: bool = True) -> int:
+    """QK and PV multiply-adds of every (query, key) pair a chunk attends:
+    4 * D flops per pair per query head."""
     cu = b.cu_seqlens_q.cpu().tolist()
     K = b.context_lens.cpu().tolist()
     pairs = 0
     for s in range(b.num_seqs):
         n = cu[s + 1] - cu[s]
-        # query i attends K - n + i + 1 keys
-        pairs += n * (K[s] - n + 1) + n * (n - 1) // 2
+        # causal: query i attends K - n + i + 1 keys; otherwise all K
+        pairs += n * (K[s] - n + 1) + n * (n - 1) // 2 if causal else n * K[s]
     return 4 * b.head_size * b.num_heads * pairs
 
 
-def bench_prefill(args, torch, pa, dev):
+def bench_prefill(args, torch, pa, dev, long_prompts: bool = False):
     """One chunked-prefill step on the Llama-7B shape: 16 sequences, a
     512-token chunk each after U{0..1536} cached tokens; the chunk's K/V are
     written (pa_cache_write), then the chunk attends its context (pa_prefill,
-    causal)."""
+    causal).  long_prompts: 8 whole prompts of 4096 tokens instead (no cached
+    prefix), and the same attention without the causal mask timed beside it."""
     import workloads
-    b = workloads.llama7b_prefill_chunks(device=dev)
+    b = (workloads.llama7b_prefill_long if long_prompts else workloads.llama7b_prefill_chunks)(
+        device=dev)
     out = torch.empty_like(b.q)
     ev = []
 
@@ -383,6 +385,24 @@ def bench_prefill(args, torch, pa, dev):
     flops = prefill_flops(b)
     achieved = flops / (kern_ms * 1e-3) / 1e12
     T = int(b.q.shape[0])
+    non_causal = None
+    if long_prompts:
+        # the cache already holds every prompt: the same launches without the mask
+        ev_nc = []
+        for _ in range(args.steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pa.prefill(b.q, b.k_cache, b.v_cache, b.block_table, b.cu_seqlens_q, b.context_lens,
+                       b.scale, b.max_seqlen_q, causal=False, out=out)
+            e1.record()
+            ev_nc.append((e0, e1))
+        torch.cuda.synchronize()
+        nc_ms = sum(a.elapsed_time(c) for a, c in ev_nc) / len(ev_nc)
+        nc_flops = prefill_flops(b, causal=False)
+        non_causal = {"kernel_ms": nc_ms, "algorithmic_flops_per_launch": nc_flops,
+                      "achieved": nc_flops / (nc_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                      "frac": nc_flops / (nc_ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS}
     cpu = None
     if not args.no_cpu_baseline:
         import numpy as np
@@ -418,23 +438,29 @@ def bench_prefill(args, torch, pa, dev):
         cpu = {"value": done / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
                "sample": f"sequence 0 ({n} queries over {K} keys), {heads} of "
                          f"{b.num_heads} heads, fp64 numpy, {dt:.1f} s"}
-    return {
+    wname = "llama7b_prefill_long" if long_prompts else "llama7b_prefill_chunks"
+    wdesc = ("llama7b_prefill_long: 8 prompts x 4096 tokens, no cached prefix, 32 = 32 kv heads, "
+             "head 128, block 16, f16" if long_prompts else
+             "llama7b_prefill_chunks: 16 seqs x 512-token chunks after U{0..1536} cached tokens, "
+             "32 = 32 kv heads, head 128, block 16, f16")
+    line = {
         "metric": "chunked prefill query tokens/s and achieved TFLOP/s (% of f16 MFMA peak), 1×MI355X",
         "value": T / (ms * 1e-3), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "llama7b_prefill_chunks: 16 seqs x 512-token chunks after "
-                               "U{0..1536} cached tokens, 32 = 32 kv heads, head 128, block 16, f16",
-                   "total_query_tokens": T, "step": "pa_cache_write + pa_prefill"},
+        "config": {"workload": wdesc, "total_query_tokens": T,
+                   "step": "pa_cache_write + pa_prefill"},
         "roofline": {"bound": "mfma", "kernel": "pa_prefill", "achieved": achieved,
                      "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_MFMA_F16_TFLOPS,
-                     "traffic": recorded_traffic("pa_prefill", "llama7b_prefill_chunks",
-                                                 kernel_source_hash()),
+                     "traffic": recorded_traffic("pa_prefill", wname, kernel_source_hash()),
                      "algorithmic_flops_per_launch": flops, "kernel_ms": kern_ms,
                      "kernel_sources": kernel_source_hash()},
         "cpu_baseline": cpu,
     }
+    if non_causal is not None:
+        line["non_causal"] = non_causal
+    return line
 
 
 class StreamProbe:
@@ -686,11 +712,13 @@ def main(argv=None):
                          "fp8_shared_prefix under per_config")
     ap.add_argument("--op", default="step",
                     choices=["step", "stream", "copy_blocks", "swap_out", "swap_in", "prefill",
-                             "fragmentation"],
+                             "prefill_long", "fragmentation"],
                     help="step: one decode step (default); stream: the HBM read probe; "
                          "copy_blocks: copy-on-write copies inside a pool; swap_out / swap_in: "
                          "blocks to / from a pinned host pool; prefill: one chunked-prefill "
-                         "step (cache write + pa_prefill); fragmentation: the host block "
+                         "step (cache write + pa_prefill); prefill_long: 8 whole 4096-token "
+                         "prompts, causal, with the unmasked attention timed beside it; "
+                         "fragmentation: the host block "
                          "manager on the how-it-works page's 100-request simulation (CPU only)")
     ap.add_argument("--unfused", action="store_true",
                     help="one-pass workloads: pa_cache_write then pa_decode instead of the "
@@ -728,8 +756,8 @@ def main(argv=None):
     if args.op == "stream":
         print(json.dumps(bench_stream(args, torch, dev)))
         return 0
-    if args.op == "prefill":
-        print(json.dumps(bench_prefill(args, torch, pa, dev)))
+    if args.op in ("prefill", "prefill_long"):
+        print(json.dumps(bench_prefill(args, torch, pa, dev, long_prompts=args.op == "prefill_long")))
         return 0
     if args.op != "step":
         print(json.dumps(bench_block_copy(args, torch, pa, dev)))

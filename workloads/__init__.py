@@ -4,7 +4,8 @@ This package only draws inputs (random values, context lengths, block tables,
 slot mappings).  It holds none of the attention arithmetic: neither the GPU
 path nor the CPU oracle is imported here, and both consume what it returns.
 """
-from .prefill import PrefillBatch, llama7b_prefill_chunks, poison_prefill, prefill_batch  # noqa: F401
+from .prefill import (PrefillBatch, llama7b_prefill_chunks, llama7b_prefill_long,  # noqa: F401
+                      poison_prefill, prefill_batch)
 from .synth import (  # noqa: F401
     Workload,
     CONFIGS,

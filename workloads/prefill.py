@@ -128,6 +128,15 @@ def llama7b_prefill_chunks(seed: int = 6, device: str = "cpu", num_seqs: int = 1
                          name="llama7b_prefill_chunks")
 
 
+def llama7b_prefill_long(seed: int = 7, device: str = "cpu", num_seqs: int = 8,
+                         prompt: int = 4096) -> PrefillBatch:
+    """Whole-prompt prefill on the Llama-7B shape (32 heads = 32 kv heads,
+    head 128, block 16, fp16): num_seqs prompts of `prompt` tokens with no
+    cached prefix, each token attending the prompt up to itself."""
+    return prefill_batch(seed, [prompt] * num_seqs, [0] * num_seqs, 32, 32, 128, 16, "f16",
+                         device=device, name="llama7b_prefill_long")
+
+
 def poison_prefill(b: PrefillBatch, covered=None, value: float = float("nan")) -> PrefillBatch:
     """Fill every cache slot outside the sequences' first covered[s] tokens
     (default: their cached prefixes, so the chunk's own slots too) with NaN
