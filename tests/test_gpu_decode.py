@@ -260,13 +260,17 @@ def _run_slots(BS):
     return [x for r in runs for x in r]
 
 
-def _write_and_compare(slots, cache_fmt, D, BS, KVH, NB, seed):
-    """pa_cache_write of random K/V into a random pool against the oracle's
-    write, both caches compared bit for bit."""
+def _write_and_compare(slots, cache_fmt, D, BS, KVH, NB, seed, in_fmt=None, sample=None):
+    """pa_cache_write of random K/V (in_fmt; default: the cache's 16-bit type,
+    f16 for fp8 caches) into a random pool against the oracle's write, both
+    caches compared bit for bit.  sample: a seeded fraction of the tokens, the
+    only ones the oracle writes, and only their slots are compared (the fp8
+    oracle quantises in fp64, one token at a time)."""
     gen = torch.Generator().manual_seed(seed)
     slots = torch.tensor(slots, dtype=torch.int32)
     T = slots.numel()
-    in_dt = torch.bfloat16 if cache_fmt == "bf16" else torch.float16
+    in_fmt = in_fmt or ("bf16" if cache_fmt == "bf16" else "f16")
+    in_dt = torch.bfloat16 if in_fmt == "bf16" else torch.float16
     k = torch.randn((T, KVH, D), generator=gen).to(in_dt)
     v = torch.randn((T, KVH, D), generator=gen).to(in_dt)
     if cache_fmt == "e4m3fn":
@@ -283,10 +287,24 @@ def _write_and_compare(slots, cache_fmt, D, BS, KVH, NB, seed):
     gk, gv = kc.to(DEV), vc.to(DEV)
     pa.cache_write(k.to(DEV), v.to(DEV), gk, gv, slots.to(DEV), k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
+    if sample is None:
+        ok, ov = oracle.cache_write(to_numpy_bits(k), to_numpy_bits(v), to_numpy_bits(kc),
+                                    to_numpy_bits(vc), slots.numpy(), BS, cache_fmt, ks, vs)
+        assert to_numpy_bits(gk).tobytes() == ok.tobytes()
+        assert to_numpy_bits(gv).tobytes() == ov.tobytes()
+        return
+    pick = np.random.default_rng(seed).random(T) < sample
+    sub = np.where(pick, slots.numpy(), -1)
     ok, ov = oracle.cache_write(to_numpy_bits(k), to_numpy_bits(v), to_numpy_bits(kc),
-                                to_numpy_bits(vc), slots.numpy(), BS, cache_fmt, ks, vs)
-    assert to_numpy_bits(gk).tobytes() == ok.tobytes()
-    assert to_numpy_bits(gv).tobytes() == ov.tobytes()
+                                to_numpy_bits(vc), sub, BS, cache_fmt, ks, vs)
+    gkn, gvn = to_numpy_bits(gk), to_numpy_bits(gv)
+    written = [int(x) for x in sub if x >= 0]
+    assert len(written) > 50
+    for sl in written:
+        b, o = divmod(sl, BS)
+        assert gkn[b, :, o].tobytes() == ok[b, :, o].tobytes(), f"K slot {sl}"
+        assert gvn[b, :, o // 4, :, o % 4].tobytes() == ov[b, :, o // 4, :, o % 4].tobytes(), \
+            f"V slot {sl}"
 
 
 @pytest.mark.parametrize("cache_fmt,D,BS", [("f16", 128, 16), ("bf16", 64, 32),
@@ -333,6 +351,25 @@ def test_cache_write_wide_grid_ragged_bit_exact(cache_fmt, D, BS):
     T = len(slots)
     assert T % 8 != 0 and -(-T // 8) * KVH >= 4096
     _write_and_compare(slots, cache_fmt, D, BS, KVH=KVH, NB=NB, seed=12)
+
+
+@pytest.mark.parametrize("wide", [False, True])
+@pytest.mark.parametrize("BS", [16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("in_fmt,cache_fmt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "e4m3fn"),
+                                              ("bf16", "e4m3fn")])
+def test_cache_write_every_kernel_bit_exact(in_fmt, cache_fmt, D, BS, wide):
+    """Every compiled cache write: input and cache types, head and block
+    sizes, one token quad per wavefront (a narrow grid) or several (a wide
+    one), with ragged prefill-like slots; bit for bit against the oracle
+    (wide fp8 writes: on an eighth of the tokens, drawn at random)."""
+    rng = np.random.default_rng(32)
+    KVH, NB = (32, 160 if BS == 16 else 100) if wide else (3, 120 if BS == 16 else 70)
+    slots = _ragged_chunk_slots(rng, BS, NB, min_tokens=1100 if wide else 300)
+    if wide:
+        assert -(-len(slots) // 8) * KVH >= 4096
+    _write_and_compare(slots, cache_fmt, D, BS, KVH=KVH, NB=NB, seed=13, in_fmt=in_fmt,
+                       sample=0.125 if wide and cache_fmt == "e4m3fn" else None)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
