@@ -29,7 +29,7 @@
 // The 16-byte granules of each K row in LDS are XOR-permuted by the key and
 // V's token-quad regions are padded by 128 bytes, so that the operand reads
 // hit every bank once.  The copies go from global memory straight into LDS
-// (global_load_lds), three stages in a ring.  Three workgroups share a CU
+// (buffer loads with the lds bit), three stages in a ring.  Three workgroups share a CU
 // (three wavefronts per SIMD: at most 168 registers each, and 3 x 52.75 KB of
 // LDS at head size 128): a wavefront alone keeps its SIMD busy little more
 // than half the time (the K/V reads from LDS, the product chains and the
@@ -308,13 +308,16 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
     // inside one cache block (block wblk of the stage, at byte offset roff0),
     // consecutive 1 KiB apart in the source.  So a stage's copy needs one
     // table entry per wavefront, and the sources are block address + per-lane
-    // offsets fixed for the loop.
+    // offsets fixed for the loop.  The block address goes into a buffer
+    // descriptor (scalar registers) and each region's offset is one 32-bit
+    // register: 64-bit lane addresses would take twice the registers, and
+    // with them the kernel spilled at three wavefronts per SIMD.
     const int half = wave & 1;
     const int roff0 = copies_k ? ((16 * half) % BS) * ROWB : ((4 * half) % (BS / 4)) * QB;
     const int rdst0 = copies_k ? wave * NREGW * 1024 : KB + half * NREGW * VREG;
     const int rstep = copies_k ? 1024 : VREG;
     const int b16 = 16 * lane;
-    int loff[NREGW];                                    // region i: source byte offset
+    uint32_t loff[NREGW];                               // region i: source byte offset
 #pragma unroll
     for (int i = 0; i < NREGW; ++i) {
       if (copies_k) {
@@ -338,12 +341,15 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
         ph = 0;
       }
       const char* base = cache + (int64_t)ph * block_stride + roff0;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, NREGW * 1024);
 #pragma unroll
       for (int i = 0; i < NREGW; ++i) {
-        const char* src = base + loff[i];
+        // named locals: an array element passed straight to the builtin made
+        // the host pass drop the kernels' launch stubs
         char* dst = &s_kv[0][0] + boff + rdst0 + i * rstep;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16,
-                                         0, 0);
+        const uint32_t lo = loff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst,
+                                                 16, lo, 0, 0, 0);
       }
     };
 
@@ -450,11 +456,11 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
     // -inf; unmasked: every key counts for every valid row and the logits go
     // straight from the products to exp2), then the accumulators meet a single
     // product path, so each product updates them in place.  The weights of
-    // both row blocks are taken first, then each V operand is read from LDS
-    // just before its two products: a wavefront holds one or two V operands
-    // instead of all NPV, which fits the kernel in the registers of three
-    // wavefronts per SIMD (the latency a wavefront leaves exposed is covered
-    // by the other two).
+    // both row blocks are taken first, then the V operands are read from LDS
+    // one ahead of their products (operand jj + 1 is in flight while jj's two
+    // products run): a wavefront holds two V operands instead of all NPV,
+    // which fits the kernel in the registers of three wavefronts per SIMD (the
+    // latency a wavefront leaves exposed is covered by the other two).
     auto compute = [&](bool masked, int t, int boff) {
       const char* kb = &s_kv[0][0] + boff;
       const char* vb = kb + KB;
@@ -546,14 +552,17 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
         }
       }
       // the PV products, V operand by V operand
+      u32x4_t va = v_operand(vb, 0);
 #pragma unroll
       for (int jj = 0; jj < NPV; ++jj) {
-        const u32x4_t va = v_operand(vb, jj);
+        u32x4_t vn = va;
+        if (jj + 1 < NPV) vn = v_operand(vb, jj + 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           acc[r][jj] = MV::qk(va, pb[r], acc[r][jj]);
           if constexpr (kSplitP) acc[r][jj] = MV::qk(va, pl[r], acc[r][jj]);
         }
+        va = vn;
       }
     };
 
