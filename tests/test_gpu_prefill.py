@@ -208,3 +208,58 @@ def test_large_scales(scale, dtype):
     b = workloads.prefill_batch(39, [9, 40, 1, 17], [20, 0, 70, 33], 8, 2, 128, 16, dtype)
     b = workloads.synth.replace(workloads.poison_prefill(b), scale=scale)
     _check(b, f"scale {scale} {dtype}")
+
+
+@pytest.mark.parametrize("dtype,cache", [("f16", ""), ("bf16", "e4m3fn")])
+def test_blocks_past_4gib_of_the_pool(dtype, cache):
+    """The batch's blocks moved to ids whose K and V tiles start past 4 GiB
+    and past 4.5 GiB of each cache (a pool of 5 GiB per cache, NaN outside the
+    moved blocks): the cache write and the prefill must give what the oracle
+    gives on the original small pool, bytes of the written blocks included."""
+    b = workloads.poison_prefill(workloads.prefill_batch(71, [64, 33, 130], [100, 300, 0], 4, 2,
+                                                         128, 16, dtype, cache))
+    what = f"pool past 4 GiB {dtype}/{cache or dtype}"
+    print(f"[prefill] {what}", flush=True)
+    ref, k_ref, v_ref = _oracle_step(b)
+    block_bytes = b.k_cache[0].numel() * b.k_cache.element_size()
+    nb_big = (5 << 30) // block_bytes
+    first = ((4 << 30) + block_bytes - 1) // block_bytes      # first block id past 4 GiB
+    table = b.block_table.clone()
+    used = sorted({int(x) for x in table.flatten().tolist() if x >= 0})
+    # spread over 4 .. 5 GiB, in reverse order of the original ids
+    new_ids = {old: first + 3 + 37 * i for i, old in enumerate(reversed(used))}
+    assert max(new_ids.values()) < nb_big
+    for s in range(table.shape[0]):
+        for j in range(table.shape[1]):
+            if table[s, j] >= 0:
+                table[s, j] = new_ids[int(table[s, j])]
+    slots = b.slot_mapping.clone()
+    BS = b.block_size
+    for i, sl in enumerate(slots.tolist()):
+        if sl >= 0:
+            slots[i] = new_ids[sl // BS] * BS + sl % BS
+    nan_code = 0x7F if cache == "e4m3fn" else None
+    big = []
+    for c in (b.k_cache, b.v_cache):
+        t = torch.empty((nb_big,) + tuple(c.shape[1:]), dtype=c.dtype, device=DEV)
+        if nan_code is None:
+            t.fill_(float("nan"))
+        else:
+            t.view(torch.uint8).fill_(nan_code)
+        idx = torch.tensor([new_ids[o] for o in used], dtype=torch.int64, device=DEV)
+        t[idx] = c[torch.tensor(used, dtype=torch.int64)].to(DEV)
+        big.append(t)
+    g = b.to(DEV)
+    table_d, slots_d = table.to(DEV), slots.to(DEV)
+    pa.cache_write(g.new_k, g.new_v, big[0], big[1], slots_d, k_scale=b.k_scale, v_scale=b.v_scale)
+    out = pa.prefill(g.q, big[0], big[1], table_d, g.cu_seqlens_q, g.context_lens, b.scale,
+                     b.max_seqlen_q, causal=True, k_scale=b.k_scale, v_scale=b.v_scale)
+    torch.cuda.synchronize()
+    atol, rtol = TOL[b.cache_dtype]
+    assert_close(as_f64(out), ref, atol, rtol, what)
+    idx = torch.tensor([new_ids[o] for o in used], dtype=torch.int64, device=DEV)
+    for t, want in ((big[0], k_ref), (big[1], v_ref)):
+        got = to_numpy_bits(t[idx].cpu())
+        assert got.tobytes() == np.ascontiguousarray(want[used]).tobytes(), what
+    del big
+    torch.cuda.empty_cache()
