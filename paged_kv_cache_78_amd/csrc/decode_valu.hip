@@ -189,10 +189,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
     part = blockIdx.z;
   } else {
     // one pass: workgroup b takes head pos % H of the sequence at position
-    // pos / H of the longest-first order (or of index order)
-    const int pos = p.order_by_length
-                        ? snake_position((int)blockIdx.x, (int)gridDim.x, p.num_cus)
-                        : (int)blockIdx.x;
+    // pos / H of the longest-first order, spread over the dies by their
+    // streaming rates (or of index order)
+    const int pos = p.order_by_length ? die_position((int)blockIdx.x, (int)gridDim.x / kDies)
+                                      : (int)blockIdx.x;
+    if (pos >= p.num_seqs * H) return;                  // a spare workgroup
     const int rank = pos / H;
     h = pos % H;
     s = p.order_by_length
@@ -471,7 +472,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
 template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid = PART ? dim3(p.num_heads, p.num_seqs, p.num_partitions)
-                        : dim3(p.num_heads * p.num_seqs, 1, 1);
+                        : dim3(p.order_by_length ? kDies * die_workgroups(p.num_heads * p.num_seqs)
+                                                 : p.num_heads * p.num_seqs,
+                               1, 1);
   hipLaunchKernelGGL((decode_valu_kernel<QT, CT, D, BS, PART, WAVES>), grid, dim3(64 * WAVES), 0,
                      stream, p);
   return hipGetLastError();

@@ -210,8 +210,11 @@ __device__ __forceinline__ int seq_by_rank(const int32_t* context_lens, int num_
   return 0;   // rank >= num_seqs: not reached for valid launches
 }
 
-// Position in the longest-first list that workgroup b takes.  Workgroups go
-// to compute units round-robin, so consecutive strata of `units` workgroups
+// Position in the longest-first list that workgroup b of a one-pass launch of
+// the matrix-core kernel takes (the vector-ALU kernel's is die_position
+// below; the die weighting made the matrix-core kernels 1-4% slower, as their
+// dies finish within 3-5% of each other).  Workgroups go to compute units
+// round-robin, so consecutive strata of `units` workgroups
 // alternate direction (a snake): each compute unit then gets one long and
 // one short item from every pair of strata instead of always the longer one.
 __device__ __forceinline__ int snake_position(int b, int total, int units) {
@@ -220,6 +223,42 @@ __device__ __forceinline__ int snake_position(int b, int total, int units) {
   if ((k & 1) == 0) return b;
   const int m = min(units, total - k * units);   // size of this stratum
   return k * units + (m - 1 - i);
+}
+
+// Position in the longest-first list that workgroup b of a one-pass launch of
+// the vector-ALU kernel takes.  Workgroups go to the dies (XCDs) round robin:
+// workgroup b runs on die b % kDies as the j-th workgroup there, j = b / kDies.
+// The odd-numbered dies of this part stream more slowly than the even ones
+// (with equal work they finish 5-10% later; a streaming read with 6% more
+// tiles on the even dies and 6% fewer on the odd ones ran 3-4% faster), so
+// positions are handed out in the order of a virtual time that advances by
+// die_cost(x) per workgroup of die x: workgroup (x, j) sits at
+// (2j + 1) die_cost(x), and its position is the number of workgroups of all
+// dies at an earlier time (equal times: the lower die first).  Every die still
+// takes the longest items first, and an even die takes die_cost(1) /
+// die_cost(0) times as many items as an odd one.  The launch has
+// kDies * die_workgroups(items) workgroups; those whose position is `items` or
+// more are spares and exit at once.
+constexpr int kDies = 8;
+__host__ __device__ constexpr int die_cost(int x) { return (x & 1) ? 53 : 47; }
+// workgroups per die: an even die's share of the items, rounded up
+__host__ __device__ constexpr int die_workgroups(int items) {
+  return (int)(((int64_t)items * die_cost(1) * 2 / (die_cost(0) + die_cost(1)) + kDies - 1) /
+               kDies);
+}
+__device__ __forceinline__ int die_position(int b, int n) {
+  const int x = b % kDies;
+  const int j = b / kDies;
+  const int t = (2 * j + 1) * die_cost(x);
+  int pos = 0;
+#pragma unroll
+  for (int y = 0; y < kDies; ++y) {
+    const int c = die_cost(y);
+    int cnt = ((t - 1) / c + 1) / 2;                     // j' with (2j' + 1) c < t
+    if (y < x && t % c == 0 && ((t / c) & 1)) ++cnt;     // the same time, lower die
+    pos += min(cnt, n);
+  }
+  return pos;
 }
 
 // ---------------------------------------------------------------------------
