@@ -184,9 +184,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   int h, s, part;
   int len_ranked = -1;                // the sequence's length, when the ranking read it
   if constexpr (PART) {
-    h = blockIdx.x;
-    s = blockIdx.y;
-    part = blockIdx.z;
+    // partitions: (head, sequence, partition) in partition-major order, the
+    // positions spread over the dies like those of a one pass
+    const int items = H * p.num_seqs * p.num_partitions;
+    const int pos = die_position((int)blockIdx.x, (int)gridDim.x / kDies);
+    if (pos >= items) return;                           // a spare workgroup
+    h = pos % H;
+    s = (pos / H) % p.num_seqs;
+    part = pos / (H * p.num_seqs);
   } else {
     // one pass: workgroup b takes head pos % H of the sequence at position
     // pos / H of the longest-first order, spread over the dies by their
@@ -471,7 +476,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
 
 template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid = PART ? dim3(p.num_heads, p.num_seqs, p.num_partitions)
+  const dim3 grid = PART ? dim3(kDies * die_workgroups(p.num_heads * p.num_seqs * p.num_partitions),
+                                1, 1)
                         : dim3(p.order_by_length ? kDies * die_workgroups(p.num_heads * p.num_seqs)
                                                  : p.num_heads * p.num_seqs,
                                1, 1);

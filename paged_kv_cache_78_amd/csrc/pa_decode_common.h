@@ -225,8 +225,9 @@ __device__ __forceinline__ int snake_position(int b, int total, int units) {
   return k * units + (m - 1 - i);
 }
 
-// Position in the longest-first list that workgroup b of a one-pass launch of
-// the vector-ALU kernel takes.  Workgroups go to the dies (XCDs) round robin:
+// Position in the list of work items (one pass: the longest-first list;
+// partitions: partition-major order) that workgroup b of a launch of the
+// vector-ALU kernel takes.  Workgroups go to the dies (XCDs) round robin:
 // workgroup b runs on die b % kDies as the j-th workgroup there, j = b / kDies.
 // The odd-numbered dies of this part stream more slowly than the even ones
 // (with equal work they finish 5-10% later; a streaming read with 6% more
@@ -235,7 +236,7 @@ __device__ __forceinline__ int snake_position(int b, int total, int units) {
 // die_cost(x) per workgroup of die x: workgroup (x, j) sits at
 // (2j + 1) die_cost(x), and its position is the number of workgroups of all
 // dies at an earlier time (equal times: the lower die first).  Every die still
-// takes the longest items first, and an even die takes die_cost(1) /
+// takes its items in list order, and an even die takes die_cost(1) /
 // die_cost(0) times as many items as an odd one.  The launch has
 // kDies * die_workgroups(items) workgroups; those whose position is `items` or
 // more are spares and exit at once.
