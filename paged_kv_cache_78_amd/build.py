@@ -27,8 +27,12 @@ PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 # with PA_LIB=paged_kv_cache_78_amd/variants/libpa_<name>.so.
 #   xlane_dpp: cross-lane reductions on DPP and v_permlane*_swap instead of
 #              ds_bpermute;
-#   table_lds: block-table window staged through LDS instead of v_readlane.
-VARIANTS = {"xlane_dpp": ["-DPA_XLANE_DPP=1"], "table_lds": ["-DPA_TABLE_LDS=1"]}
+#   table_lds: block-table window staged through LDS instead of v_readlane;
+#   plain_grid: the vector-ALU kernel's launches past their die-order limit
+#               (every launch: 3-D partition grid, one pass in index order),
+#               so that the tests reach that path.
+VARIANTS = {"xlane_dpp": ["-DPA_XLANE_DPP=1"], "table_lds": ["-DPA_TABLE_LDS=1"],
+            "plain_grid": ["-DPA_DIE_MAX_ITEMS=0"]}
 VARIANT_FILES = ("decode_valu.hip", "decode_mfma.hip")
 VARIANT_DIR = os.path.join(PKG, "variants")
 ARCH = "gfx950"

@@ -184,14 +184,20 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   int h, s, part;
   int len_ranked = -1;                // the sequence's length, when the ranking read it
   if constexpr (PART) {
-    // partitions: (head, sequence, partition) in partition-major order, the
-    // positions spread over the dies like those of a one pass
-    const int items = H * p.num_seqs * p.num_partitions;
-    const int pos = die_position((int)blockIdx.x, (int)gridDim.x / kDies);
-    if (pos >= items) return;                           // a spare workgroup
-    h = pos % H;
-    s = (pos / H) % p.num_seqs;
-    part = pos / (H * p.num_seqs);
+    if (p.die_order) {
+      // partitions: (head, sequence, partition) in partition-major order, the
+      // positions spread over the dies like those of a one pass
+      const int items = H * p.num_seqs * p.num_partitions;
+      const int pos = die_position((int)blockIdx.x, (int)gridDim.x / kDies);
+      if (pos >= items) return;                         // a spare workgroup
+      h = pos % H;
+      s = (pos / H) % p.num_seqs;
+      part = pos / (H * p.num_seqs);
+    } else {
+      h = blockIdx.x;
+      s = blockIdx.y;
+      part = blockIdx.z;
+    }
   } else {
     // one pass: workgroup b takes head pos % H of the sequence at position
     // pos / H of the longest-first order, spread over the dies by their
@@ -474,10 +480,22 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
   }
 }
 
+// Launches take the die order up to kDieMaxItems items (the positions'
+// virtual times stay within 32 bits); beyond that, partitions take the plain
+// 3-D grid and a one pass the index order.
+#ifndef PA_DIE_MAX_ITEMS
+#define PA_DIE_MAX_ITEMS (int64_t(1) << 27)
+#endif
+constexpr int64_t kDieMaxItems = PA_DIE_MAX_ITEMS;
+
 template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
-hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid = PART ? dim3(kDies * die_workgroups(p.num_heads * p.num_seqs * p.num_partitions),
-                                1, 1)
+hipError_t launch_one(const DecodeParams& pa, hipStream_t stream) {
+  DecodeParams p = pa;
+  const int64_t part_items = (int64_t)p.num_heads * p.num_seqs * p.num_partitions;
+  p.die_order = PART && part_items <= kDieMaxItems ? 1 : 0;
+  if (!PART && (int64_t)p.num_heads * p.num_seqs > kDieMaxItems) p.order_by_length = 0;
+  const dim3 grid = PART ? (p.die_order ? dim3(kDies * die_workgroups((int)part_items), 1, 1)
+                                        : dim3(p.num_heads, p.num_seqs, p.num_partitions))
                         : dim3(p.order_by_length ? kDies * die_workgroups(p.num_heads * p.num_seqs)
                                                  : p.num_heads * p.num_seqs,
                                1, 1);

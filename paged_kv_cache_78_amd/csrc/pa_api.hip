@@ -98,6 +98,7 @@ pa::DecodeParams make_params(const void* q, const void* k_cache, const void* v_c
   // every workgroup re-derives the order from context_lens: worth it while
   // that scan is short
   p.order_by_length = num_seqs <= kMaxOrderedSeqs ? 1 : 0;
+  p.die_order = 0;
   p.num_cus = compute_units();
   return p;
 }

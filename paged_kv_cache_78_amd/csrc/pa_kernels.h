@@ -31,6 +31,7 @@ struct DecodeParams {
   int32_t partition_size;    // tokens per partition (partitioned), else 0
   int32_t num_partitions;    // NP (partitioned), else 1
   int32_t order_by_length;   // one pass: dispatch the longest contexts first
+  int32_t die_order;         // vector-ALU partitions: a 1-D grid through die_position
   int32_t num_cus;           // compute units of the device (dispatch order)
   // fused append (one pass only): sequence s's new token k_new/v_new[s]
   // ([KVH, D] rows, token stride kv_token_stride) is stored at

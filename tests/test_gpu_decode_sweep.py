@@ -75,3 +75,46 @@ def test_every_decode_kernel(qd, cache, D, BS, G, mode):
         assert_close(as_f64(out), ref, atol, rtol, what)
         assert to_numpy_bits(g.k_cache).tobytes() == kc.tobytes(), what
         assert to_numpy_bits(g.v_cache).tobytes() == vc.tobytes(), what
+
+
+@pytest.mark.parametrize("mode", ["one_pass", "partitioned", "append"])
+def test_vector_alu_plain_grid(mode):
+    """The vector-ALU kernel's launches beyond the die order's item limit (a
+    3-D partition grid; one pass in index order), reached through the library
+    built with that limit at zero: the same parity as the default build."""
+    import os
+    import paged_kv_cache_78_amd.binding as B
+    path = os.path.join(os.path.dirname(B.__file__), "variants", "libpa_plain_grid.so")
+    what = f"plain grid {mode}"
+    print(f"[decode sweep] {what}", flush=True)
+    saved_path, saved_lib = B._LIB_PATH, B._lib
+    try:
+        B._LIB_PATH, B._lib = path, None
+        for qd in ("f16", "bf16"):
+            wl = _workload(qd, qd, 128, 16, 1)
+            g = wl.to(DEV)
+            atol, rtol = tol_of(wl)
+            if mode == "one_pass":
+                out = pa.decode(g.q, g.k_cache, g.v_cache, g.block_table, g.context_lens, wl.scale)
+                torch.cuda.synchronize()
+                assert_close(as_f64(out), oracle_decode(wl), atol, rtol, what)
+            elif mode == "partitioned":
+                out = pa.decode_partitioned(g.q, g.k_cache, g.v_cache, g.block_table,
+                                            g.context_lens, wl.scale, 32, int(wl.context_lens.max()))
+                torch.cuda.synchronize()
+                assert_close(as_f64(out), oracle_decode(wl), atol, rtol, what)
+            else:
+                out = pa.decode_append(g.q, g.new_k, g.new_v, g.k_cache, g.v_cache, g.slot_mapping,
+                                       g.block_table, g.context_lens, wl.scale)
+                torch.cuda.synchronize()
+                a = oracle_arrays(wl)
+                ref, kc, vc = oracle.decode_append(a["q"], to_numpy_bits(wl.new_k),
+                                                   to_numpy_bits(wl.new_v), a["k"], a["v"],
+                                                   wl.slot_mapping.cpu().numpy(), a["table"],
+                                                   a["lens"], wl.scale, wl.num_kv_heads,
+                                                   wl.block_size, wl.q_dtype, wl.cache_dtype)
+                assert_close(as_f64(out), ref, atol, rtol, what)
+                assert to_numpy_bits(g.k_cache).tobytes() == kc.tobytes(), what
+                assert to_numpy_bits(g.v_cache).tobytes() == vc.tobytes(), what
+    finally:
+        B._LIB_PATH, B._lib = saved_path, saved_lib
