@@ -489,8 +489,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_valu_kernel(const DecodePar
 constexpr int64_t kDieMaxItems = PA_DIE_MAX_ITEMS;
 
 template <typename QT, typename CT, int D, int BS, bool PART, int WAVES>
-hipError_t launch_one(const DecodeParams& pa, hipStream_t stream) {
-  DecodeParams p = pa;
+hipError_t launch_one(const DecodeParams& params, hipStream_t stream) {
+  DecodeParams p = params;
   const int64_t part_items = (int64_t)p.num_heads * p.num_seqs * p.num_partitions;
   p.die_order = PART && part_items <= kDieMaxItems ? 1 : 0;
   if (!PART && (int64_t)p.num_heads * p.num_seqs > kDieMaxItems) p.order_by_length = 0;
