@@ -102,11 +102,12 @@ def test_negative_and_zero_scale(scale, G):
     assert_close(as_f64(out), oracle_decode(wl), atol, rtol, f"scale {scale} G={G}")
 
 
-@pytest.mark.parametrize("S,G", [(300, 1), (300, 8), (1100, 1), (1100, 4)])
+@pytest.mark.parametrize("S,G", [(300, 1), (300, 8), (1024, 1), (1025, 1), (1100, 1), (1100, 4)])
 def test_many_sequences(S, G):
     """More sequences than one lane set caches for the longest-first ranking
     (256: lengths are read again in its second pass) and than the ranking
-    covers at all (1024: index order), one head per kv head and grouped;
+    covers at all (1024, the last count it orders; beyond: index order), one
+    head per kv head and grouped;
     every row against the oracle (the output starts as NaN, so a sequence
     the ranking skipped cannot pass)."""
     if G == 1:
