@@ -179,12 +179,29 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
     }
   }
 
+  // Q^T operands: row block r's column n, dims 32 cc + 8 g .. +7 of chunk cc.
+  // qready: they were loaded at the end of the last unit for this one.  With
+  // bf16 queries or fp8 caches the next unit's Q is loaded at the end of each
+  // unit, so its latency passes during the epilogue and the unit start
+  // (interleaved timing: bf16 -2.0 to -2.5%, fp8 caches -2.5 to -3.8%); with
+  // f16 queries over f16 caches the same was 0.8-1.5% slower, and Q is loaded
+  // at the unit start.
+  constexpr bool kQNext = !(__is_same(QT, F16) && ESZ == 2);
+  u32x4_t qb[R][NQK];
+  bool qready = false;
   for (int round = 0;; ++round) {
     const int jq = round * SPX + ((round & 1) ? SPX - 1 - slot : slot);
     if (jq >= units_x) break;
     // the last unit's LDS (stage buffers, table windows, the bad-entry flags)
-    // is free once every wavefront is here
-    __syncthreads();
+    // is free once every wavefront is here: its LDS accesses are complete
+    // (its copies were all waited for in its last stages), and the bare
+    // barrier leaves the next unit's Q loads in flight
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const bool qpre = qready;
+    qready = false;
     int s, c, kvh;
     bool live;
     if (ranked) {
@@ -285,8 +302,6 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
       continue;
     }
 
-    // Q^T operands: row block r's column n, dims 32 cc + 8 g .. +7 of chunk cc
-    u32x4_t qb[R][NQK];
 
     // ---- staging: the stage's K and V tiles, copied global -> LDS ----
     // A copy instruction puts lane i's 16 bytes at LDS base + 16 i: each
@@ -606,14 +621,16 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
       stage_copy(0, 0, entries_pre(0));
       if (wave == 0 && nstages > 3) window_copy(0);
     }
+    if (!qpre) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const char* qrow = reinterpret_cast<const char*>(p.q) +
-                         ((int64_t)(q0 + qi[r]) * q_token_stride + (int64_t)hh[r] * D) * 2;
+      for (int r = 0; r < R; ++r) {
+        const char* qrow = reinterpret_cast<const char*>(p.q) +
+                           ((int64_t)(q0 + qi[r]) * q_token_stride + (int64_t)hh[r] * D) * 2;
 #pragma unroll
-      for (int cc = 0; cc < NQK; ++cc)
-        qb[r][cc] = ok_row[r] ? *reinterpret_cast<const u32x4_t*>(qrow + (32 * cc + 8 * g) * 2)
-                              : u32x4_t{0u, 0u, 0u, 0u};
+        for (int cc = 0; cc < NQK; ++cc)
+          qb[r][cc] = ok_row[r] ? *reinterpret_cast<const u32x4_t*>(qrow + (32 * cc + 8 * g) * 2)
+                                : u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     if (p.qk_scale_log2 < 0.0f) {
@@ -686,10 +703,67 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
       stage_end(t);
     }
 
+    // The next unit's Q, into the registers this unit no longer needs, when
+    // that unit will compute (the same checks as at its start; nothing is
+    // loaded for a unit that writes no rows or only NaN rows)
+    if constexpr (kQNext) {
+      const int round_n = round + 1;
+      const int jn = round_n * SPX + ((round_n & 1) ? SPX - 1 - slot : slot);
+      if (jn < units_x) {
+        int sn, cn, kn;
+        bool ln;
+        if (ranked) {
+          const uint64_t hit =
+              __builtin_amdgcn_ballot_w64(rk_mult > 0 && rk_pos <= jn &&
+                                          jn < rk_pos + rk_mult * chunks);
+          ln = hit != 0;
+          const int gl = ln ? (int)__builtin_ctzll(hit) : 0;
+          const int local = jn - __builtin_amdgcn_readlane(rk_pos, gl);
+          sn = gl;
+          cn = chunks - 1 - local % chunks;
+          kn = ((x - sn * KVH) % kXcds + kXcds) % kXcds + kXcds * (local / chunks);
+        } else {
+          const int item = (jn / chunks) * kXcds + x;
+          ln = item < p.num_seqs * KVH;
+          cn = chunks - 1 - jn % chunks;
+          sn = ln ? item / KVH : 0;
+          kn = item % KVH;
+        }
+        if (ln) {
+          const int32_t a0 = p.cu_seqlens_q[sn];
+          const int32_t a1 = p.cu_seqlens_q[sn + 1];
+          const int Kn = p.context_lens[sn];
+          const int nqn = a1 - a0;
+          const int rowsn = nqn * G;
+          const int row0n = cn * ROWS;
+          if (a0 >= 0 && a1 <= total_q && nqn > 0 && row0n < rowsn &&
+              !(Kn < 0 || Kn > MB * BS || nqn > max_seqlen_q)) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const int row = row0n + wave * 16 * R + 16 * r + n;
+              const bool okr = row < rowsn;
+              const int qin = okr ? row / G : 0;
+              const int hn = kn * G + (okr ? row % G : 0);
+              const char* qrow = reinterpret_cast<const char*>(p.q) +
+                                 ((int64_t)(a0 + qin) * q_token_stride + (int64_t)hn * D) * 2;
+#pragma unroll
+              for (int cc = 0; cc < NQK; ++cc)
+                qb[r][cc] = okr ? *reinterpret_cast<const u32x4_t*>(qrow + (32 * cc + 8 * g) * 2)
+                                : u32x4_t{0u, 0u, 0u, 0u};
+            }
+            qready = true;
+          }
+        }
+      }
+    }
     // A bad table entry met by any wavefront (each checks the blocks it
     // copies) makes the workgroup's rows NaN; a row with no key gives zeros.
+    // The barrier waits for LDS only, leaving the next unit's Q in flight.
     s_bad[wave] = bad_entry ? 1 : 0;
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const bool bad_any = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
     float4_t o[R][NPV];
 #pragma unroll
