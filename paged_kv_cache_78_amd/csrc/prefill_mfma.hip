@@ -179,6 +179,28 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
     }
   }
 
+  // Unit j of this XCD's queue: its sequence s, chunk c (the chunk with the
+  // most keys first) and kv head; false past the items.
+  auto unit_at = [&](int j, int& s, int& c, int& kvh) -> bool {
+    if (ranked) {
+      const uint64_t hit =
+          __builtin_amdgcn_ballot_w64(rk_mult > 0 && rk_pos <= j && j < rk_pos + rk_mult * chunks);
+      const bool live = hit != 0;
+      const int gl = live ? (int)__builtin_ctzll(hit) : 0;
+      const int local = j - __builtin_amdgcn_readlane(rk_pos, gl);
+      s = gl;
+      c = chunks - 1 - local % chunks;
+      kvh = ((x - s * KVH) % kXcds + kXcds) % kXcds + kXcds * (local / chunks);
+      return live;
+    }
+    const int item = (j / chunks) * kXcds + x;
+    const bool live = item < p.num_seqs * KVH;
+    c = chunks - 1 - j % chunks;
+    s = live ? item / KVH : 0;
+    kvh = item % KVH;
+    return live;
+  };
+
   // Q^T operands: row block r's column n, dims 32 cc + 8 g .. +7 of chunk cc.
   // qready: they were loaded at the end of the last unit for this one.  With
   // bf16 queries or fp8 caches the next unit's Q is loaded at the end of each
@@ -203,24 +225,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
     const bool qpre = qready;
     qready = false;
     int s, c, kvh;
-    bool live;
-    if (ranked) {
-      const uint64_t hit =
-          __builtin_amdgcn_ballot_w64(rk_mult > 0 && rk_pos <= jq &&
-                                      jq < rk_pos + rk_mult * chunks);
-      live = hit != 0;
-      const int gl = live ? (int)__builtin_ctzll(hit) : 0;
-      const int local = jq - __builtin_amdgcn_readlane(rk_pos, gl);
-      s = gl;
-      c = chunks - 1 - local % chunks;
-      kvh = ((x - s * KVH) % kXcds + kXcds) % kXcds + kXcds * (local / chunks);
-    } else {
-      const int item = (jq / chunks) * kXcds + x;
-      live = item < p.num_seqs * KVH;
-      c = chunks - 1 - jq % chunks;
-      s = live ? item / KVH : 0;
-      kvh = item % KVH;
-    }
+    const bool live = unit_at(jq, s, c, kvh);
 
     // The sequence's lengths and the table entries of its first three stages
     // are loaded at once (indices clamped into the row; entries past the
@@ -711,25 +716,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(3)))
       const int jn = round_n * SPX + ((round_n & 1) ? SPX - 1 - slot : slot);
       if (jn < units_x) {
         int sn, cn, kn;
-        bool ln;
-        if (ranked) {
-          const uint64_t hit =
-              __builtin_amdgcn_ballot_w64(rk_mult > 0 && rk_pos <= jn &&
-                                          jn < rk_pos + rk_mult * chunks);
-          ln = hit != 0;
-          const int gl = ln ? (int)__builtin_ctzll(hit) : 0;
-          const int local = jn - __builtin_amdgcn_readlane(rk_pos, gl);
-          sn = gl;
-          cn = chunks - 1 - local % chunks;
-          kn = ((x - sn * KVH) % kXcds + kXcds) % kXcds + kXcds * (local / chunks);
-        } else {
-          const int item = (jn / chunks) * kXcds + x;
-          ln = item < p.num_seqs * KVH;
-          cn = chunks - 1 - jn % chunks;
-          sn = ln ? item / KVH : 0;
-          kn = item % KVH;
-        }
-        if (ln) {
+        if (unit_at(jn, sn, cn, kn)) {
           const int32_t a0 = p.cu_seqlens_q[sn];
           const int32_t a1 = p.cu_seqlens_q[sn + 1];
           const int Kn = p.context_lens[sn];
