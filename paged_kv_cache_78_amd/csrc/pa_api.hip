@@ -1,5 +1,6 @@
 // C ABI of libpa: argument validation and kernel selection.  No device code
 // lives here; every check happens before anything is launched.
+#include <atomic>
 #include <math.h>
 
 #include "../../include/pa.h"
@@ -15,18 +16,19 @@ constexpr int kMaxOrderedSeqs = 1024;
 constexpr int kMaxPartitions = 15360;
 
 // Compute units of the current device, asked once per device (256 if the
-// runtime cannot say).
+// runtime cannot say).  Callers on several host threads may ask at once: the
+// cache is atomic (they may each ask the runtime; all store the same value).
 int compute_units() {
-  static int cache[64];   // 0 = not asked yet
+  static std::atomic<int> cache[64];   // 0 = not asked yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 // The kernels move rows with 16-byte loads and stores.
